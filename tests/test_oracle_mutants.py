@@ -1,0 +1,67 @@
+"""The pins are strong enough: each plausible mistake planted in a copy of the
+oracle's C source (compiled to a temporary library, on the CPU) makes at
+least one pin fail.  Each mutant runs in a child process, so a mutant that
+reads out of bounds cannot take the test runner down."""
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+import oracle
+
+ROOT = Path(__file__).resolve().parents[1]
+PINS = Path(__file__).resolve().parent / "oracle_pins.py"
+
+# (name, exact text in oracle_sgemm.c, replacement)
+MUTANTS = [
+    ("drop_last_term", "for (int64_t t = 0; t < k; ++t) {\n            const double a",
+     "for (int64_t t = 0; t < k - 1; ++t) {\n            const double a"),
+    ("drop_first_term", "for (int64_t t = 0; t < k; ++t) {\n            const double a",
+     "for (int64_t t = 1; t < k; ++t) {\n            const double a"),
+    ("wrong_sign", "acc[j] += p;", "acc[j] -= p;"),
+    ("a_transposed", "jb->A[i * jb->lda + t]", "jb->A[t * jb->lda + i]"),
+    ("b_transposed", "const double p = a * (double)brow[j];",
+     "const double p = a * (double)jb->B[j * jb->ldb + t];"),
+    ("b_row_index_i", "const float *brow = jb->B + t * jb->ldb;",
+     "const float *brow = jb->B + i * jb->ldb;"),
+    ("alpha_ignored", "double r = use_ab ? jb->alpha * acc[j] : 0.0;",
+     "double r = use_ab ? acc[j] : 0.0;"),
+    ("beta_sign", "if (jb->beta != 0.0) r += jb->beta * (double)crow[j];",
+     "if (jb->beta != 0.0) r -= jb->beta * (double)crow[j];"),
+    ("beta_zero_reads_c", "if (jb->beta != 0.0) r += jb->beta * (double)crow[j];",
+     "r += jb->beta * (double)crow[j];"),
+    ("alpha_zero_reads_ab", "const int use_ab = (k > 0 && jb->alpha != 0.0);",
+     "const int use_ab = (k > 0);"),
+    ("float_accumulator", "const double p = a * (double)brow[j];",
+     "const double p = (double)(float)(a * (double)brow[j]); acc[j] = (float)acc[j];"),
+    ("g_signed", "gacc[j] += fabs(p);", "gacc[j] += p;"),
+    ("row_list_ignored", "const int64_t i = jb->rows ? jb->rows[s] : s;",
+     "const int64_t i = s;"),
+    ("points_drop_last", "for (int64_t t = 0; t < k; ++t) {\n                const double prod",
+     "for (int64_t t = 0; t + 1 < k; ++t) {\n                const double prod"),
+    ("points_transposed_b", "(double)B[t * ldb + j]", "(double)B[j * ldb + t]"),
+    ("points_beta_sign", "if (db != 0.0) r += db * (double)C[i * ldc + j];",
+     "if (db != 0.0) r -= db * (double)C[i * ldc + j];"),
+    ("c_pad_written", "for (int64_t j = 0; j < n; ++j) {\n        double r",
+     "for (int64_t j = 0; j < jb->ldc; ++j) {\n        double r"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = oracle.SRC.read_text()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = oracle.build(mutated, tmp_path / "liboracle_mutant.so")
+    res = subprocess.run([sys.executable, str(PINS), str(lib)], cwd=ROOT,
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode != 0, f"mutant {name} passed every pin:\n{res.stdout}"
+
+
+def test_unmutated_source_passes(tmp_path):
+    lib = oracle.build(oracle.SRC, tmp_path / "liboracle_copy.so")
+    res = subprocess.run([sys.executable, str(PINS), str(lib)], cwd=ROOT,
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout + res.stderr
