@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""SGEMM benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kernel KIND]
+
+One step is one call of the hot path (C = alpha*A*B + beta*C through the C
+ABI) on seeded synthetic operands already resident in HBM.  W untimed steps,
+then exactly K steps timed with HIP events on the stream the kernels run on.
+Prints ONE JSON line: throughput in TFLOP/s (2mnk per step), the roofline
+object of the GEMM kernel (which is the only kernel a step launches for the
+default workload, so its average duration is the step time), the CPU oracle
+timed on a bounded sample of the same workload, and secondary measurements
+of the other workloads.
+
+Only the CPU-baseline leg imports the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+DEFAULT_WORKLOAD = "sgemm_2048x2048x2048"
+METRIC = "SGEMM TFLOPS at 2048^3 and 8192^3 FP32; % of MI355X FP32 peak"
+
+
+def source_digest() -> str:
+    """Hash of the kernel sources and header; traffic counters recorded for
+    another digest describe other code and are not reported."""
+    h = hashlib.sha256()
+    files = sorted((ROOT / "hpc_tiling_amd" / "csrc").glob("*")) + sorted((ROOT / "include").glob("*.h"))
+    for f in files:
+        h.update(f.name.encode())
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.txt, if
+    it was measured on the current sources."""
+    p = ROOT / "profiles" / f"traffic_{kernel}_{workload}.txt"
+    if not p.exists():
+        return None
+    kv = {}
+    for line in p.read_text().splitlines():
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def sclk_mhz():
+    """Current shader clock from sysfs, when readable."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(f):
+                if "*" in line:
+                    return float(line.split(":")[1].strip().rstrip("*").strip().rstrip("Mhz").strip())
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def make_step(kind, w, Av, Bv, Cv, ws):
+    import hpc_tiling_amd as hta
+    alpha, beta = w.alpha, w.beta
+    if kind == "mfma":
+        return lambda: hta.sgemm(Av, Bv, Cv, alpha, beta)
+    if kind == "valu":
+        return lambda: hta.sgemm_valu(Av, Bv, Cv, alpha, beta)
+    if kind == "splitk":
+        return lambda: hta.sgemm_splitk(Av, Bv, Cv, alpha, beta, splits=0, workspace=ws)
+    if kind.startswith("mfma_cfg"):
+        cfg = int(kind[len("mfma_cfg"):])
+        return lambda: hta.sgemm(Av, Bv, Cv, alpha, beta, config=cfg)
+    raise ValueError(kind)
+
+
+def setup(w, kind):
+    import torch
+    import hpc_tiling_amd as hta
+    import synth
+    A, B, C = synth.operands(w)
+    dev = torch.device("cuda:0")
+    Ad, Bd, Cd = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+    ws = None
+    if kind == "splitk":
+        ws = hta.splitk_workspace(w.m, w.n, w.k, 0, device=dev)
+    torch.cuda.synchronize()
+    return (A, B, C), (Ad, Bd, Cd), make_step(kind, w, Ad[:, :w.k], Bd[:, :w.n], Cd[:, :w.n], ws)
+
+
+def time_steps(step, steps, warmup):
+    """Seconds for exactly `steps` calls after `warmup` untimed ones, measured
+    with events on the current stream (the stream the kernels are launched on)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / 1e3
+
+
+def cpu_baseline(w, host, budget_s):
+    """The oracle on whole output rows of the same workload, as many rows as
+    fit the time budget (estimated from a first small batch)."""
+    import numpy as np
+    import oracle
+    import synth
+    A, B, C = host
+    orc = oracle.get()
+    threads = oracle.default_threads()
+    probe = synth.sample_rows([w.wid, 1234], w.m, min(w.m, max(threads, 8)))
+    t0 = time.perf_counter()
+    orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, rows=probe,
+              want_g=True, threads=threads)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    nrows = int(min(w.m, max(len(probe), budget_s / max(per_row, 1e-9))))
+    nrows = max(threads, (nrows // threads) * threads) if nrows < w.m else w.m
+    rows = synth.sample_rows([w.wid, 4321], w.m, nrows)
+    t0 = time.perf_counter()
+    orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, rows=rows,
+              want_g=True, threads=threads)
+    dt = time.perf_counter() - t0
+    used = int(min(threads, len(rows)))
+    flops = 2.0 * len(rows) * w.n * w.k
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+        "sample": (f"{len(rows)} of {w.m} output rows of {w.name} (all {w.n} columns, full k="
+                   f"{w.k}); FP64 accumulation, also summing |A_it B_tj|; {dt:.2f} s"),
+        "seconds": dt, "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def secondary(kinds_workloads, reps=10):
+    """TFLOP/s of other (kernel, workload) pairs, a few calls each."""
+    import torch
+    import synth
+    from hpc_tiling_amd import perfmodel as pm
+    out = []
+    for kind, name in kinds_workloads:
+        w = synth.workload(name)
+        host, dev, step = setup(w, kind)
+        n = max(2, min(reps, int(2e13 // max(w.flops, 1))))
+        dt = time_steps(step, n, warmup=2)
+        tf = pm.tflops(w.m, w.n, w.k, dt, reps=n)
+        out.append({"workload": name, "kernel": kind, "ms_per_call": 1e3 * dt / n,
+                    "tflops": tf, "frac_of_fp32_peak": tf * 1e12 / pm.PEAK_FP32_MFMA})
+        del host, dev, step
+        torch.cuda.empty_cache()
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--kernel", default="mfma", help="mfma | valu | splitk | mfma_cfgN")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the oracle leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU "
+              "(one MI355X); multi-GPU runs are out of scope.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                          "launches": 5}), flush=True)
+        return 0
+
+    import synth
+    from hpc_tiling_amd import perfmodel as pm
+
+    w = synth.workload(args.workload)
+    kind = args.kernel
+    print(f"[bench] {kind} {w.name}: generating operands", file=sys.stderr, flush=True)
+    host, dev, step = setup(w, kind)
+    sclk_before = sclk_mhz()
+    print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    dt = time_steps(step, args.steps, args.warmup)
+    sclk_after = sclk_mhz()
+    ms = 1e3 * dt / args.steps
+    value = pm.tflops(w.m, w.n, w.k, dt, reps=args.steps)
+
+    dominant = {"mfma": "sgemm_mfma_kernel", "valu": "sgemm_valu_kernel",
+                "splitk": "sgemm_mfma_kernel (split-K partials)"}.get(kind, "sgemm_mfma_kernel")
+    roof = {
+        "bound": "mfma" if kind != "valu" else "alu",
+        "kernel": dominant,
+        "achieved": value,
+        "peak": (pm.PEAK_FP32_MFMA if kind != "valu" else pm.PEAK_FP32_VALU_SCALAR) / 1e12,
+        "unit": "TFLOP/s",
+        "frac": None,
+        "traffic": read_traffic(kind, w.name),
+        "algorithmic_flop_per_launch": w.flops,
+        "avg_launch_ms": ms,
+        "timing": "HIP events on the launch stream over the timed steps",
+    }
+    roof["frac"] = roof["achieved"] / roof["peak"]
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded uniform[-1,1) float32 operands, resident in HBM)",
+        "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k, "lda": w.lda, "ldb": w.ldb,
+                   "ldc": w.ldc, "alpha": w.alpha, "beta": w.beta, "kernel": kind,
+                   "layout": "row-major"},
+        "frac_of_fp32_peak": value * 1e12 / pm.PEAK_FP32_MFMA,
+        "sclk_mhz": {"before": sclk_before, "after": sclk_after},
+        "roofline": roof,
+    }
+    del dev, step
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        print("[bench] secondary workloads", file=sys.stderr, flush=True)
+        pairs = [("mfma", "sgemm_8192x8192x8192_ab"), ("mfma", "sgemm_tails_3001x4997x1023"),
+                 ("splitk", "sgemm_splitk_512x512x262144"), ("valu", "sgemm_2048x2048x2048"),
+                 ("mfma", "sgemm_256x256x256")]
+        line["secondary"] = secondary(pairs)
+
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, host, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,229 @@
+"""Python binding of libmi_sgemm (single-precision GEMM for MI355X / gfx950).
+
+Thin ctypes layer over the C ABI declared in ``include/mi_sgemm.h``: the
+functions named like the C entry points (``mi_sgemm``, ``mi_sgemm_valu``,
+``mi_sgemm_splitk``, ...) take the same arguments (device pointers as
+integers, the stream as an integer handle); the ``sgemm*`` helpers marshal
+torch tensors to them.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback path.  Importing raises ImportError when the
+library has not been built (``python hpc_tiling_amd/build.py``).
+
+torch is used for device memory and streams only, and is imported lazily.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+__all__ = [
+    "LIB_PATH", "lib", "MiSgemmError", "Plan",
+    "mi_sgemm", "mi_sgemm_valu", "mi_sgemm_splitk", "mi_sgemm_splitk_workspace_bytes",
+    "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
+    "sgemm", "sgemm_valu", "sgemm_splitk", "splitk_workspace",
+    "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = Path(__file__).resolve().parent / "libmi_sgemm.so"
+
+SUCCESS = 0
+ERROR_INVALID_VALUE = 1
+ERROR_INVALID_LD = 2
+ERROR_NULL_POINTER = 3
+ERROR_WORKSPACE = 4
+ERROR_LAUNCH = 5
+ERROR_DEVICE = 6
+
+KERNEL_MFMA = 0
+KERNEL_VALU = 1
+KERNEL_SPLITK = 2
+
+EXPORTED_SYMBOLS = (
+    "mi_sgemm", "mi_sgemm_valu", "mi_sgemm_splitk_workspace_bytes", "mi_sgemm_splitk",
+    "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
+)
+
+if not LIB_PATH.exists():
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python hpc_tiling_amd/build.py` "
+        "(the HIP library is required; there is no other implementation)")
+
+lib = ctypes.CDLL(str(LIB_PATH))
+
+_i, _f, _vp, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_GEMM_ARGS = [_i, _i, _i, _f, _vp, _i, _vp, _i, _f, _vp, _i]
+
+
+class Plan(ctypes.Structure):
+    """Mirror of struct mi_sgemm_plan."""
+    _fields_ = [
+        ("kernel", _i), ("config", _i),
+        ("tile_m", _i), ("tile_n", _i), ("tile_k", _i),
+        ("micro_m", _i), ("micro_n", _i), ("threads", _i),
+        ("tiles_m", _i), ("tiles_n", _i), ("workgroups", ctypes.c_longlong),
+        ("splits", _i), ("k_per_split", _i), ("big_iterations", _i),
+        ("small_iterations", _i), ("fma_per_small_iteration", _i),
+        ("outputs_per_thread", _i), ("a_elements_per_big_iteration", _i),
+        ("b_elements_per_big_iteration", _i), ("group_m", _i), ("vector_loads", _i),
+        ("workspace_bytes", _sz),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+lib.mi_sgemm.argtypes = _GEMM_ARGS + [_vp]
+lib.mi_sgemm.restype = _i
+lib.mi_sgemm_valu.argtypes = _GEMM_ARGS + [_vp]
+lib.mi_sgemm_valu.restype = _i
+lib.mi_sgemm_with_config.argtypes = [_i, _i] + _GEMM_ARGS + [_vp]
+lib.mi_sgemm_with_config.restype = _i
+lib.mi_sgemm_splitk_workspace_bytes.argtypes = [_i, _i, _i, _i]
+lib.mi_sgemm_splitk_workspace_bytes.restype = _sz
+lib.mi_sgemm_splitk.argtypes = _GEMM_ARGS + [_i, _vp, _sz, _vp]
+lib.mi_sgemm_splitk.restype = _i
+lib.mi_status_string.argtypes = [_i]
+lib.mi_status_string.restype = ctypes.c_char_p
+lib.mi_sgemm_get_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(Plan)]
+lib.mi_sgemm_get_plan.restype = _i
+lib.mi_sgemm_config_count.argtypes = [_i]
+lib.mi_sgemm_config_count.restype = _i
+
+
+class MiSgemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mi_status_string(status)} (status {status})")
+
+
+# ---------------------------------------------------------------------------
+# C entry points, same names and arguments
+# ---------------------------------------------------------------------------
+def mi_sgemm(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    return lib.mi_sgemm(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def mi_sgemm_valu(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    return lib.mi_sgemm_valu(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def mi_sgemm_with_config(kernel, config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                         stream=None) -> int:
+    return lib.mi_sgemm_with_config(kernel, config, m, n, k, alpha, A, lda, B, ldb, beta, C,
+                                    ldc, stream)
+
+
+def mi_sgemm_splitk_workspace_bytes(m, n, k, splits=0) -> int:
+    return lib.mi_sgemm_splitk_workspace_bytes(m, n, k, splits)
+
+
+def mi_sgemm_splitk(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws, ws_bytes,
+                    stream=None) -> int:
+    return lib.mi_sgemm_splitk(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws,
+                               ws_bytes, stream)
+
+
+def mi_status_string(status: int) -> str:
+    return lib.mi_status_string(status).decode()
+
+
+def mi_sgemm_get_plan(kernel, config, m, n, k, splits=0) -> dict:
+    p = Plan()
+    st = lib.mi_sgemm_get_plan(kernel, config, m, n, k, splits, ctypes.byref(p))
+    if st != SUCCESS:
+        raise MiSgemmError(st, "mi_sgemm_get_plan")
+    return p.as_dict()
+
+
+def mi_sgemm_config_count(kernel) -> int:
+    return lib.mi_sgemm_config_count(kernel)
+
+
+# ---------------------------------------------------------------------------
+# torch tensor helpers
+# ---------------------------------------------------------------------------
+def _operand(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major (unit column stride)")
+    ld = max(t.stride(0), t.shape[1], 1) if t.shape[0] > 1 else max(t.shape[1], 1)
+    return t.data_ptr(), ld
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _prepare(A, B, C, beta):
+    import torch
+    m, k = A.shape
+    k2, n = B.shape
+    if k2 != k:
+        raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if C is None:
+        if beta != 0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((m, n), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (m, n):
+        raise ValueError(f"C is {tuple(C.shape)}, expected {(m, n)}")
+    pa, lda = _operand(A, "A")
+    pb, ldb = _operand(B, "B")
+    pc, ldc = _operand(C, "C")
+    return m, n, k, pa, lda, pb, ldb, C, pc, ldc
+
+
+def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
+    """C <- alpha * A @ B + beta * C on the matrix cores; returns C.
+    A (m x k), B (k x n), C (m x n): float32 device tensors, row-major
+    (row strides are passed as leading dimensions)."""
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
+    s = _stream(stream)
+    if config is None:
+        st = lib.mi_sgemm(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, s)
+    else:
+        st = lib.mi_sgemm_with_config(KERNEL_MFMA, config, m, n, k, alpha, pa, lda, pb, ldb,
+                                      beta, pc, ldc, s)
+    if st != SUCCESS:
+        raise MiSgemmError(st, "mi_sgemm")
+    return C
+
+
+def sgemm_valu(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
+    """Same as sgemm, on the register-tiled VALU kernel."""
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
+    st = lib.mi_sgemm_valu(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, _stream(stream))
+    if st != SUCCESS:
+        raise MiSgemmError(st, "mi_sgemm_valu")
+    return C
+
+
+def splitk_workspace(m, n, k, splits=0, device="cuda"):
+    """A device workspace tensor large enough for mi_sgemm_splitk."""
+    import torch
+    nbytes = mi_sgemm_splitk_workspace_bytes(m, n, k, splits)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, stream=None):
+    """Same as sgemm with the k range split into slices; `workspace` is a
+    device tensor of at least mi_sgemm_splitk_workspace_bytes bytes (allocated
+    here when None)."""
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
+    if workspace is None:
+        workspace = splitk_workspace(m, n, k, splits, device=A.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mi_sgemm_splitk(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
+                             workspace.data_ptr(), ws_bytes, _stream(stream))
+    if st != SUCCESS:
+        raise MiSgemmError(st, "mi_sgemm_splitk")
+    return C

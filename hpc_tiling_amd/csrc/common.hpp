@@ -1,0 +1,74 @@
+// common.hpp -- argument block and workgroup-order helpers shared by the
+// SGEMM kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// MI355X places workgroups on its 8 XCDs (each with a private L2) round-robin
+// by workgroup id.
+constexpr int kXcds = 8;
+
+// Everything a GEMM kernel needs; passed by value as the single kernel
+// argument.  Leading dimensions and slice strides are 64-bit so that row
+// offsets never overflow.
+struct GemmArgs {
+    int m, n, k;
+    float alpha, beta;
+    const float *A;
+    long long lda;
+    const float *B;
+    long long ldb;
+    float *C;
+    long long ldc;
+    int tiles_m, tiles_n;  // C tiles along m and n
+    int group_m;           // height (in tiles) of one group of the grouped order
+    int k_per_split;       // split-K: length of a k slice (multiple of the k step)
+    float *ws;             // split-K: partials, slice s at ws + s * ws_slice
+    long long ws_slice;    // split-K: floats per slice (>= m * n, multiple of 64)
+    int c_vec;             // 1 when C is 16-byte aligned and ldc % 4 == 0
+};
+
+// Renumbers workgroups so that each XCD owns one contiguous range of logical
+// ids: hardware id w runs on XCD w % 8 as that XCD's (w / 8)-th workgroup.
+// The map is a bijection of [0, count) for every count.
+__device__ __forceinline__ int xcd_contiguous(int w, int count) {
+    const int q = count / kXcds, r = count % kXcds;
+    const int x = w % kXcds, idx = w / kXcds;
+    return x * q + (x < r ? x : r) + idx;
+}
+
+// Grouped tile order (page "gemm优化", section on L2 swizzle): consecutive
+// logical ids walk down a group of `group_m` tile rows before moving to the
+// next tile column, so neighbouring workgroups share both B columns and A
+// rows in L2.  A bijection of [0, tiles_m * tiles_n).
+__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n,
+                                             int group_m, int &tm, int &tn) {
+    const int per_group = group_m * tiles_n;
+    const int g = id / per_group;
+    const int first = g * group_m;
+    const int rows = min(tiles_m - first, group_m);
+    const int local = id - g * per_group;
+    tm = first + local % rows;
+    tn = local / rows;
+}
+
+// Four consecutive floats src[0..3]; elements at index >= valid read as 0
+// (never dereferenced).  `vec` allows one 16-byte load when all 4 are valid.
+template <bool VEC>
+__device__ __forceinline__ f32x4 load4_masked(const float *src, int valid) {
+    if (VEC && valid >= 4) return *reinterpret_cast<const f32x4 *>(src);
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (valid > 0) v[0] = src[0];
+    if (valid > 1) v[1] = src[1];
+    if (valid > 2) v[2] = src[2];
+    if (valid > 3) v[3] = src[3];
+    return v;
+}
+
+}  // namespace mi

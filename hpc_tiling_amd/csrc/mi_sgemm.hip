@@ -1,0 +1,367 @@
+// mi_sgemm.hip -- C-ABI entry points: argument checks, planning and launch
+// of the SGEMM kernels for gfx950.  Declarations and semantics are in
+// include/mi_sgemm.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdint>
+#include <cstring>
+
+#include "mi_sgemm.h"
+#include "sgemm_mfma.hpp"
+#include "sgemm_valu.hpp"
+#include "splitk.hpp"
+
+namespace mi {
+namespace {
+
+using KernelFn = void (*)(GemmArgs);
+
+// ---------------------------------------------------------------------------
+// Tile configurations of the matrix-core kernel.
+// ---------------------------------------------------------------------------
+struct MfmaConfig {
+    int bm, bn, bk, wgm, wgn;
+    KernelFn vec, scalar;              // full-k kernels
+    KernelFn split_vec, split_scalar;  // split-K partial kernels (may be null)
+};
+
+template <class T>
+constexpr MfmaConfig make_cfg(bool with_split) {
+    return MfmaConfig{T::BM, T::BN, T::BK, T::WGM, T::WGN,
+                      &sgemm_mfma_kernel<T, true, false>, &sgemm_mfma_kernel<T, false, false>,
+                      with_split ? &sgemm_mfma_kernel<T, true, true> : nullptr,
+                      with_split ? &sgemm_mfma_kernel<T, false, true> : nullptr};
+}
+
+using Cfg128x128x16 = MfmaTile<128, 128, 16, 2, 2>;
+using Cfg128x128x32 = MfmaTile<128, 128, 32, 2, 2>;
+using Cfg128x64x32 = MfmaTile<128, 64, 32, 2, 2>;
+using Cfg256x128x16 = MfmaTile<256, 128, 16, 2, 2>;
+using Cfg128x128x16w8 = MfmaTile<128, 128, 16, 2, 4>;
+using Cfg64x64x32 = MfmaTile<64, 64, 32, 2, 2>;
+
+const MfmaConfig kMfmaConfigs[] = {
+    make_cfg<Cfg128x128x16>(true),     // 0
+    make_cfg<Cfg128x128x32>(true),     // 1
+    make_cfg<Cfg128x64x32>(false),     // 2
+    make_cfg<Cfg256x128x16>(false),    // 3
+    make_cfg<Cfg128x128x16w8>(false),  // 4
+    make_cfg<Cfg64x64x32>(false),      // 5
+};
+constexpr int kNumMfmaConfigs = sizeof(kMfmaConfigs) / sizeof(kMfmaConfigs[0]);
+constexpr int kSplitConfig = 0;  // tile configuration of the split-K partial kernel
+
+constexpr int kGroupM = 8;  // grouped-order height (the pages use groups of 8)
+
+int choose_mfma_config(int m, int n, int k) {
+    (void)m; (void)n; (void)k;
+    return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K sizing.
+// ---------------------------------------------------------------------------
+struct SplitPlan {
+    int splits;        // slices actually used
+    int k_per_split;   // multiple of the k step
+    long long slice;   // floats per workspace slice
+    size_t bytes;      // workspace bytes including alignment slack
+};
+
+constexpr size_t kWsAlign = 256;
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+SplitPlan plan_split(int m, int n, int k, int splits) {
+    SplitPlan sp{0, 0, 0, 0};
+    if (m <= 0 || n <= 0 || k <= 0) return sp;
+    const MfmaConfig &c = kMfmaConfigs[kSplitConfig];
+    const long long tiles = ceil_div(m, c.bm) * ceil_div(n, c.bn);
+    long long want = splits;
+    if (want == 0) {
+        // Aim at about four workgroups per CU (256 CUs), with slices of at
+        // least 8 k steps.
+        const long long target_wg = 1024;
+        want = ceil_div(target_wg, tiles);
+        const long long max_by_k = ceil_div(k, 8LL * c.bk);
+        if (want > max_by_k) want = max_by_k;
+        if (want > 256) want = 256;
+        if (want < 1) want = 1;
+    }
+    long long kps = ceil_div(ceil_div(k, want), c.bk) * c.bk;
+    sp.k_per_split = (int)kps;
+    sp.splits = (int)ceil_div(k, kps);
+    sp.slice = ceil_div((long long)m * n, 64) * 64;
+    sp.bytes = (size_t)sp.splits * (size_t)sp.slice * sizeof(float) + kWsAlign;
+    return sp;
+}
+
+// ---------------------------------------------------------------------------
+// Checks shared by every entry point.
+// ---------------------------------------------------------------------------
+int check_sizes(int m, int n, int k, int lda, int ldb, int ldc) {
+    if (m < 0 || n < 0 || k < 0) return MI_SGEMM_ERROR_INVALID_VALUE;
+    if (lda < (k > 1 ? k : 1) || ldb < (n > 1 ? n : 1) || ldc < (n > 1 ? n : 1))
+        return MI_SGEMM_ERROR_INVALID_LD;
+    return MI_SGEMM_SUCCESS;
+}
+
+int check_pointers(int m, int n, int k, float alpha, const float *A, const float *B,
+                   const float *C) {
+    if (m == 0 || n == 0) return MI_SGEMM_SUCCESS;
+    if (!C) return MI_SGEMM_ERROR_NULL_POINTER;
+    if (k > 0 && alpha != 0.f && (!A || !B)) return MI_SGEMM_ERROR_NULL_POINTER;
+    return MI_SGEMM_SUCCESS;
+}
+
+// The kernels are built for gfx950 only: refuse anything else up front.
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MI_SGEMM_ERROR_DEVICE;
+    static std::atomic<signed char> state[128];  // 0 unknown, 1 gfx950, -1 other
+    if (dev >= 128) return MI_SGEMM_ERROR_DEVICE;
+    const signed char s = state[dev].load(std::memory_order_acquire);
+    if (s != 0) return s > 0 ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MI_SGEMM_ERROR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    state[dev].store(ok ? 1 : -1, std::memory_order_release);
+    return ok ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_DEVICE;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool vector_ok(const float *A, int lda, const float *B, int ldb) {
+    return aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0;
+}
+
+int launch(KernelFn fn, long long grid, int threads, hipStream_t stream, GemmArgs args) {
+    if (grid <= 0) return MI_SGEMM_SUCCESS;
+    if (grid > INT_MAX) return MI_SGEMM_ERROR_INVALID_VALUE;
+    void *kargs[] = {&args};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid),
+                                   dim3(threads), kargs, 0, stream);
+    if (e != hipSuccess) return MI_SGEMM_ERROR_LAUNCH;
+    e = hipGetLastError();
+    return e == hipSuccess ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_LAUNCH;
+}
+
+int launch_scale(int m, int n, float beta, float *C, int ldc, hipStream_t stream) {
+    const long long total = (long long)m * n;
+    long long blocks = ceil_div(total, 256);
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(scale_c_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, m, n,
+                       beta, C, (long long)ldc);
+    return hipGetLastError() == hipSuccess ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_LAUNCH;
+}
+
+GemmArgs base_args(int m, int n, int k, float alpha, const float *A, int lda, const float *B,
+                   int ldb, float beta, float *C, int ldc) {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.m = m; a.n = n; a.k = k;
+    a.alpha = alpha; a.beta = beta;
+    a.A = A; a.lda = lda; a.B = B; a.ldb = ldb; a.C = C; a.ldc = ldc;
+    a.group_m = kGroupM;
+    a.c_vec = aligned16(C) && ldc % 4 == 0;
+    return a;
+}
+
+// Common prologue of the compute entry points.  Returns SUCCESS with
+// *done = true when the call is complete without a GEMM kernel.
+int prologue(int m, int n, int k, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, hipStream_t stream, bool *done) {
+    *done = true;
+    int st = check_sizes(m, n, k, lda, ldb, ldc);
+    if (st) return st;
+    st = check_pointers(m, n, k, alpha, A, B, C);
+    if (st) return st;
+    if (m == 0 || n == 0) return MI_SGEMM_SUCCESS;
+    st = check_device();
+    if (st) return st;
+    if (k == 0 || alpha == 0.f) return launch_scale(m, n, beta, C, ldc, stream);
+    *done = false;
+    return MI_SGEMM_SUCCESS;
+}
+
+int run_mfma(int config, int m, int n, int k, float alpha, const float *A, int lda,
+             const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+    if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bool done;
+    int st = prologue(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, &done);
+    if (st || done) return st;
+    const int id = config < 0 ? choose_mfma_config(m, n, k) : config;
+    const MfmaConfig &c = kMfmaConfigs[id];
+    GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
+    a.tiles_m = (int)ceil_div(m, c.bm);
+    a.tiles_n = (int)ceil_div(n, c.bn);
+    const long long grid = (long long)a.tiles_m * a.tiles_n;
+    return launch(vector_ok(A, lda, B, ldb) ? c.vec : c.scalar, grid, 64 * c.wgm * c.wgn, s, a);
+}
+
+int run_valu(int config, int m, int n, int k, float alpha, const float *A, int lda,
+             const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+    if (config > 0) return MI_SGEMM_ERROR_INVALID_VALUE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bool done;
+    int st = prologue(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, &done);
+    if (st || done) return st;
+    GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
+    a.tiles_m = (int)ceil_div(m, ValuTile::BM);
+    a.tiles_n = (int)ceil_div(n, ValuTile::BN);
+    const long long grid = (long long)a.tiles_m * a.tiles_n;
+    KernelFn fn = vector_ok(A, lda, B, ldb) ? &sgemm_valu_kernel<true> : &sgemm_valu_kernel<false>;
+    return launch(fn, grid, ValuTile::NT, s, a);
+}
+
+}  // namespace
+}  // namespace mi
+
+using namespace mi;
+
+extern "C" {
+
+int mi_sgemm(int m, int n, int k, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream) {
+    return run_mfma(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int mi_sgemm_valu(int m, int n, int k, float alpha, const float *A, int lda, const float *B,
+                  int ldb, float beta, float *C, int ldc, void *stream) {
+    return run_valu(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int mi_sgemm_with_config(int kernel, int config, int m, int n, int k, float alpha,
+                         const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                         int ldc, void *stream) {
+    if (kernel == MI_SGEMM_KERNEL_MFMA)
+        return run_mfma(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    if (kernel == MI_SGEMM_KERNEL_VALU)
+        return run_valu(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return MI_SGEMM_ERROR_INVALID_VALUE;
+}
+
+size_t mi_sgemm_splitk_workspace_bytes(int m, int n, int k, int splits) {
+    if (m < 0 || n < 0 || k < 0 || splits < 0 || splits > k) return 0;
+    return plan_split(m, n, k, splits).bytes;
+}
+
+int mi_sgemm_splitk(int m, int n, int k, float alpha, const float *A, int lda, const float *B,
+                    int ldb, float beta, float *C, int ldc, int splits, void *ws,
+                    size_t ws_bytes, void *stream) {
+    int st = check_sizes(m, n, k, lda, ldb, ldc);
+    if (st) return st;
+    if (splits < 0 || splits > k) return MI_SGEMM_ERROR_INVALID_VALUE;
+    st = check_pointers(m, n, k, alpha, A, B, C);
+    if (st) return st;
+    if (m == 0 || n == 0) return MI_SGEMM_SUCCESS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k == 0 || alpha == 0.f) {
+        st = check_device();
+        return st ? st : launch_scale(m, n, beta, C, ldc, s);
+    }
+    const SplitPlan sp = plan_split(m, n, k, splits);
+    if (!ws || ws_bytes < sp.bytes) return MI_SGEMM_ERROR_WORKSPACE;
+    st = check_device();
+    if (st) return st;
+
+    float *wsa = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + kWsAlign - 1) &
+                                           ~(uintptr_t)(kWsAlign - 1));
+    const MfmaConfig &c = kMfmaConfigs[kSplitConfig];
+    GemmArgs a = base_args(m, n, k, 1.f, A, lda, B, ldb, 0.f, nullptr, ldc);
+    a.tiles_m = (int)ceil_div(m, c.bm);
+    a.tiles_n = (int)ceil_div(n, c.bn);
+    a.k_per_split = sp.k_per_split;
+    a.ws = wsa;
+    a.ws_slice = sp.slice;
+    const long long grid = (long long)a.tiles_m * a.tiles_n * sp.splits;
+    st = launch(vector_ok(A, lda, B, ldb) ? c.split_vec : c.split_scalar, grid,
+                64 * c.wgm * c.wgn, s, a);
+    if (st) return st;
+
+    const long long chunks = ceil_div((long long)m * n, 64);
+    const long long blocks = ceil_div(chunks, 4);
+    if (blocks > INT_MAX) return MI_SGEMM_ERROR_INVALID_VALUE;
+    hipLaunchKernelGGL(splitk_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const float *)wsa, sp.slice, sp.splits, m, n, alpha, beta, C,
+                       (long long)ldc);
+    return hipGetLastError() == hipSuccess ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_LAUNCH;
+}
+
+const char *mi_status_string(int status) {
+    switch (status) {
+        case MI_SGEMM_SUCCESS: return "success";
+        case MI_SGEMM_ERROR_INVALID_VALUE: return "invalid value (size, split count or id)";
+        case MI_SGEMM_ERROR_INVALID_LD: return "leading dimension smaller than the row width";
+        case MI_SGEMM_ERROR_NULL_POINTER: return "null pointer for an operand that is used";
+        case MI_SGEMM_ERROR_WORKSPACE: return "workspace missing or too small";
+        case MI_SGEMM_ERROR_LAUNCH: return "kernel launch failed";
+        case MI_SGEMM_ERROR_DEVICE: return "no current gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+int mi_sgemm_config_count(int kernel) {
+    if (kernel == MI_SGEMM_KERNEL_MFMA) return kNumMfmaConfigs;
+    if (kernel == MI_SGEMM_KERNEL_VALU) return 1;
+    if (kernel == MI_SGEMM_KERNEL_SPLITK) return 1;
+    return 0;
+}
+
+int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
+                      mi_sgemm_plan *plan) {
+    if (!plan || m < 0 || n < 0 || k < 0) return MI_SGEMM_ERROR_INVALID_VALUE;
+    std::memset(plan, 0, sizeof(*plan));
+    plan->kernel = kernel;
+    plan->group_m = kGroupM;
+    plan->vector_loads = 1;
+    plan->splits = 1;
+    plan->k_per_split = k;
+    if (kernel == MI_SGEMM_KERNEL_VALU) {
+        if (config > 0) return MI_SGEMM_ERROR_INVALID_VALUE;
+        plan->config = 0;
+        plan->tile_m = ValuTile::BM; plan->tile_n = ValuTile::BN; plan->tile_k = ValuTile::BK;
+        plan->micro_m = ValuTile::RM; plan->micro_n = ValuTile::RN;
+        plan->threads = ValuTile::NT;
+        plan->small_iterations = ValuTile::BK;
+        plan->fma_per_small_iteration = ValuTile::RM * ValuTile::RN;
+        plan->outputs_per_thread = ValuTile::RM * ValuTile::RN;
+    } else if (kernel == MI_SGEMM_KERNEL_MFMA || kernel == MI_SGEMM_KERNEL_SPLITK) {
+        int id;
+        if (kernel == MI_SGEMM_KERNEL_SPLITK) {
+            if (config > 0 || splits < 0 || splits > k) return MI_SGEMM_ERROR_INVALID_VALUE;
+            id = kSplitConfig;
+        } else {
+            if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
+            id = config < 0 ? choose_mfma_config(m, n, k) : config;
+        }
+        const MfmaConfig &c = kMfmaConfigs[id];
+        plan->config = id;
+        plan->tile_m = c.bm; plan->tile_n = c.bn; plan->tile_k = c.bk;
+        plan->micro_m = c.bm / c.wgm; plan->micro_n = c.bn / c.wgn;
+        plan->threads = 64 * c.wgm * c.wgn;
+        plan->small_iterations = c.bk / 2;
+        plan->fma_per_small_iteration = (plan->micro_m / 32) * (plan->micro_n / 32);
+        plan->outputs_per_thread = plan->micro_m * plan->micro_n / 64;
+        if (kernel == MI_SGEMM_KERNEL_SPLITK) {
+            const SplitPlan sp = plan_split(m, n, k, splits);
+            plan->splits = sp.splits;
+            plan->k_per_split = sp.k_per_split;
+            plan->workspace_bytes = sp.bytes;
+        }
+    } else {
+        return MI_SGEMM_ERROR_INVALID_VALUE;
+    }
+    plan->tiles_m = (int)ceil_div(m, plan->tile_m);
+    plan->tiles_n = (int)ceil_div(n, plan->tile_n);
+    plan->workgroups = (long long)plan->tiles_m * plan->tiles_n * (plan->splits > 0 ? plan->splits : 1);
+    plan->big_iterations = (int)ceil_div(plan->k_per_split, plan->tile_k);
+    plan->a_elements_per_big_iteration = plan->tile_m * plan->tile_k;
+    plan->b_elements_per_big_iteration = plan->tile_k * plan->tile_n;
+    return MI_SGEMM_SUCCESS;
+}
+
+}  // extern "C"

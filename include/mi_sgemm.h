@@ -1,0 +1,187 @@
+/*
+ * mi_sgemm.h -- single-precision GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (every compute entry point)
+ * -------------------------------------
+ *     C <- alpha * A * B + beta * C,     C_ij = sum_{t=0}^{k-1} A_it * B_tj
+ * The sum is the GEMM of page "GEMM优化原理" (hatrix.site), section 问题定义,
+ * eq. 1 (A is m x k, B is k x n, C is m x n); the two scalars are those of the
+ * kernel signature shown on page "gemm优化" (blog.lightlisten.com), section
+ * 性能分析, read with the usual BLAS meaning.
+ *
+ * Layout.  All matrices are row-major with a leading dimension (the distance,
+ * in elements, between the starts of consecutive rows):
+ *     A_it = A[i*lda + t],   B_tj = B[t*ldb + j],   C_ij = C[i*ldc + j].
+ * Elements beyond the logical width of a row (the padding up to ld) are never
+ * read or written.  Pointers need no particular alignment and ld values need
+ * not be multiples of 4: 16-byte vector loads are used when A and B are
+ * 16-byte aligned with lda and ldb multiples of 4, element loads otherwise.
+ *
+ * Memory and streams.  A, B, C and the workspace are device memory owned by
+ * the caller; the library never allocates or frees memory in these calls.
+ * `stream` is a hipStream_t (NULL = the null stream) of the current device.
+ * Compute calls are asynchronous: they return once the kernels are enqueued.
+ * C must not overlap A, B or the workspace.  Results are deterministic: the
+ * same call on the same inputs gives the same bits.
+ *
+ * Special cases.
+ *  - m == 0 or n == 0: nothing is done (no pointer is touched).
+ *  - k == 0 or alpha == 0: C <- beta * C; A and B are not read.
+ *  - beta == 0: C is written without being read (NaN or Inf in C do not
+ *    propagate).
+ *
+ * Errors.  Every argument is checked before anything is enqueued; on an error
+ * nothing is written.  Return values are mi_status codes; mi_status_string()
+ * gives a text.  A failure reported by the HIP runtime at launch time maps to
+ * MI_SGEMM_ERROR_LAUNCH; a current device that is not gfx950 (or no device)
+ * maps to MI_SGEMM_ERROR_DEVICE.
+ */
+#ifndef MI_SGEMM_H
+#define MI_SGEMM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mi_status {
+    MI_SGEMM_SUCCESS = 0,
+    MI_SGEMM_ERROR_INVALID_VALUE = 1, /* m, n or k < 0; splits < 0 or > k;
+                                         unknown kernel or config id; grid too large */
+    MI_SGEMM_ERROR_INVALID_LD = 2,    /* lda < max(1,k), ldb < max(1,n) or ldc < max(1,n) */
+    MI_SGEMM_ERROR_NULL_POINTER = 3,  /* NULL for an operand that would be read or written */
+    MI_SGEMM_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than required */
+    MI_SGEMM_ERROR_LAUNCH = 5,        /* the HIP runtime rejected a kernel launch */
+    MI_SGEMM_ERROR_DEVICE = 6         /* no current HIP device, or it is not gfx950 */
+} mi_status;
+
+/*
+ * mi_sgemm -- the matrix-core path.
+ * Blocked through the memory hierarchy as described on page "GEMM优化原理",
+ * sections "从 global memory 到 shared memory 再到 register" and
+ * "prefetch 和双缓冲": workgroup tiles of C staged through double-buffered LDS,
+ * per-wave tiles accumulated by FP32 MFMA instructions, and a grouped,
+ * XCD-aware workgroup order for L2 reuse (page "gemm优化", section
+ * 杂项：预取缓存1， Swizzle 增强L2缓存命中).
+ * Arguments: m, n, k >= 0 sizes; alpha, beta scalars; A, B read-only inputs;
+ * C input (when beta != 0) and output; lda, ldb, ldc leading dimensions in
+ * elements; stream a hipStream_t or NULL.  Returns a mi_status.
+ */
+int mi_sgemm(int m, int n, int k, float alpha,
+             const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream);
+
+/*
+ * mi_sgemm_valu -- the register-tiled VALU path, kept as a measured
+ * comparison.  It follows the worked example of page "GEMM优化原理", section
+ * 一个具体的例子: 128 x 128 workgroup tiles, k step 8, 256 threads each owning
+ * an 8 x 8 block of C updated by outer products of 8 A and 8 B values
+ * (page aerisun.top, section "Register Tiling 与线程内复用"), with a
+ * double-buffered LDS stage.  Same arguments, semantics and errors as
+ * mi_sgemm.
+ */
+int mi_sgemm_valu(int m, int n, int k, float alpha,
+                  const float *A, int lda, const float *B, int ldb,
+                  float beta, float *C, int ldc, void *stream);
+
+/*
+ * mi_sgemm_splitk_workspace_bytes -- bytes of device workspace that
+ * mi_sgemm_splitk needs for these sizes and this split request (splits = 0
+ * asks the library to choose).  Returns 0 when no workspace is needed
+ * (m == 0, n == 0 or k == 0) and also for invalid arguments (m, n, k < 0,
+ * splits < 0 or splits > k).
+ */
+size_t mi_sgemm_splitk_workspace_bytes(int m, int n, int k, int splits);
+
+/*
+ * mi_sgemm_splitk -- the same product with the k range cut into S slices.
+ * The sum over t of page "GEMM优化原理" (section 基于 shared memory 计算,
+ * the "big iteration" over K) is split: workgroup (tile, s) sums its slice of
+ * t into raw FP32 partials in the workspace, then a second kernel adds the S
+ * partials of every C element -- each lane summing some slices, then a
+ * cross-lane wavefront reduction (page aerisun.top, sections
+ * "先在线程内累加，再交换部分和" and "Warp shuffle 的数据交换") -- and applies
+ * alpha and beta.  splits: requested S (0 = choose automatically; the
+ * library may use fewer slices so that each is a whole number of k steps).
+ * ws / ws_bytes: caller-owned device workspace of at least
+ * mi_sgemm_splitk_workspace_bytes(m, n, k, splits) bytes, 256-byte aligned
+ * for best speed; its contents on return are unspecified.  Two calls that
+ * share a workspace must be ordered on one stream.  Other arguments and
+ * errors as mi_sgemm, plus MI_SGEMM_ERROR_WORKSPACE.
+ */
+int mi_sgemm_splitk(int m, int n, int k, float alpha,
+                    const float *A, int lda, const float *B, int ldb,
+                    float beta, float *C, int ldc,
+                    int splits, void *ws, size_t ws_bytes, void *stream);
+
+/* Text for a mi_status value (a static string; never NULL). */
+const char *mi_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Planning queries (host only, no GPU needed) and forced configurations.
+ * ------------------------------------------------------------------------ */
+
+typedef enum mi_kernel {
+    MI_SGEMM_KERNEL_MFMA = 0,
+    MI_SGEMM_KERNEL_VALU = 1,
+    MI_SGEMM_KERNEL_SPLITK = 2
+} mi_kernel;
+
+/*
+ * Launch geometry chosen for a call, in the vocabulary of page
+ * "GEMM优化原理", section 问题定义, eq. 2 (b_m, b_n, b_k tiles; r_m x r_n per
+ * thread; M x N blocks; K big iterations of b_k; b_k small iterations).
+ */
+typedef struct mi_sgemm_plan {
+    int kernel;            /* mi_kernel */
+    int config;            /* tile configuration id (see mi_sgemm_config_count) */
+    int tile_m, tile_n, tile_k;   /* b_m, b_n, b_k */
+    int micro_m, micro_n;  /* VALU: r_m, r_n per thread; MFMA: per-wave tile */
+    int threads;           /* threads per workgroup */
+    int tiles_m, tiles_n;  /* M = ceil(m / b_m), N = ceil(n / b_n) */
+    long long workgroups;  /* grid size of the main kernel */
+    int splits;            /* K slices (1 when not split) */
+    int k_per_split;       /* length of every slice but possibly the last */
+    int big_iterations;    /* b_k steps per workgroup: ceil(k_per_split / b_k) */
+    int small_iterations;  /* per big iteration: b_k (VALU) or b_k / 2 (MFMA k steps) */
+    int fma_per_small_iteration; /* per thread (VALU: r_m r_n FMAs) or per wave
+                                    (MFMA: 32x32x2 instructions) */
+    int outputs_per_thread;      /* C elements accumulated by one thread/lane */
+    int a_elements_per_big_iteration; /* b_m * b_k */
+    int b_elements_per_big_iteration; /* b_k * b_n */
+    int group_m;           /* height, in tiles, of the grouped workgroup order */
+    int vector_loads;      /* 1 when 16-byte loads of A and B are used */
+    size_t workspace_bytes;
+} mi_sgemm_plan;
+
+/*
+ * mi_sgemm_get_plan -- fills *plan with what a call of `kernel` would launch
+ * for these sizes (lda/ldb multiples of 4 and aligned pointers assumed for
+ * vector_loads; config = -1 for the automatic choice, else a forced id;
+ * splits as for mi_sgemm_splitk, ignored otherwise).  Touches no GPU.
+ * Returns MI_SGEMM_SUCCESS or MI_SGEMM_ERROR_INVALID_VALUE.
+ */
+int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
+                      mi_sgemm_plan *plan);
+
+/* Number of tile configurations of `kernel` that can be forced (ids 0..count-1). */
+int mi_sgemm_config_count(int kernel);
+
+/*
+ * mi_sgemm_with_config -- mi_sgemm / mi_sgemm_valu with a forced tile
+ * configuration (for measured comparisons of tilings and for tests that
+ * cover every configuration).  kernel is MI_SGEMM_KERNEL_MFMA or
+ * MI_SGEMM_KERNEL_VALU; config < 0 means the automatic choice.  Same
+ * semantics and errors as mi_sgemm; an unknown config gives
+ * MI_SGEMM_ERROR_INVALID_VALUE.
+ */
+int mi_sgemm_with_config(int kernel, int config, int m, int n, int k, float alpha,
+                         const float *A, int lda, const float *B, int ldb,
+                         float beta, float *C, int ldc, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_SGEMM_H */

@@ -1,0 +1,151 @@
+"""Host-side checks of the C-ABI library: it loads, exports every function the
+header declares, plans launches as the pages' worked example says, and rejects
+bad arguments before touching any GPU.  No compute call runs here."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import hpc_tiling_amd as hta
+
+ROOT = Path(__file__).resolve().parents[1]
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+def _declared_functions():
+    names = set()
+    for h in (ROOT / "include").glob("*.h"):
+        text = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(mi_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def _golden(name):
+    out = {}
+    for line in (GOLDEN / name).read_text().splitlines():
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        parts = line.split()
+        out[parts[0]] = parts[1:] if len(parts) > 2 else parts[1]
+    return out
+
+
+def test_header_declares_expected_functions():
+    assert _declared_functions() == set(hta.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(str(hta.LIB_PATH))
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_status_strings():
+    for st in range(7):
+        assert hta.mi_status_string(st) != "unknown status"
+    assert hta.mi_status_string(99) == "unknown status"
+
+
+def test_valu_plan_is_the_worked_example():
+    g = {k: int(v) for k, v in _golden("worked_example_2048.txt").items()}
+    p = hta.mi_sgemm_get_plan(hta.KERNEL_VALU, -1, g["m"], g["n"], g["k"])
+    for key in ("tile_m", "tile_n", "tile_k", "micro_m", "micro_n", "workgroups", "threads",
+                "outputs_per_thread", "big_iterations", "small_iterations",
+                "fma_per_small_iteration", "a_elements_per_big_iteration",
+                "b_elements_per_big_iteration"):
+        assert p[key] == g[key], key
+    assert p["tile_m"] * p["tile_n"] == g["c_elements_per_block"]
+
+
+def test_mfma_plan_geometry():
+    for cfg in range(hta.mi_sgemm_config_count(hta.KERNEL_MFMA)):
+        p = hta.mi_sgemm_get_plan(hta.KERNEL_MFMA, cfg, 3001, 4997, 1023)
+        assert p["tiles_m"] == -(-3001 // p["tile_m"])
+        assert p["tiles_n"] == -(-4997 // p["tile_n"])
+        assert p["workgroups"] == p["tiles_m"] * p["tiles_n"]
+        assert p["big_iterations"] == -(-1023 // p["tile_k"])
+        assert p["micro_m"] % 32 == 0 and p["micro_n"] % 32 == 0
+        assert p["threads"] % 64 == 0
+        waves = p["threads"] // 64
+        assert p["outputs_per_thread"] * 64 * waves == p["tile_m"] * p["tile_n"]
+
+
+def test_splitk_plan_and_workspace():
+    p = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, 512, 512, 262144, 0)
+    assert p["splits"] * p["k_per_split"] >= 262144
+    assert (p["splits"] - 1) * p["k_per_split"] < 262144
+    assert p["k_per_split"] % p["tile_k"] == 0
+    ws = hta.mi_sgemm_splitk_workspace_bytes(512, 512, 262144, 0)
+    assert ws == p["workspace_bytes"] >= p["splits"] * 512 * 512 * 4
+    # explicit split counts: never more slices than asked, each slice whole k steps
+    for req in (1, 2, 3, 7, 64, 1000):
+        q = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, 100, 70, 5000, req)
+        assert 1 <= q["splits"] <= req
+        assert q["splits"] * q["k_per_split"] >= 5000 > (q["splits"] - 1) * q["k_per_split"]
+    assert hta.mi_sgemm_splitk_workspace_bytes(4, 4, 8, 9) == 0   # splits > k
+    assert hta.mi_sgemm_splitk_workspace_bytes(0, 4, 8, 0) == 0
+    assert hta.mi_sgemm_splitk_workspace_bytes(4, 4, 0, 0) == 0
+
+
+def test_bad_plan_requests():
+    with pytest.raises(hta.MiSgemmError):
+        hta.mi_sgemm_get_plan(7, -1, 1, 1, 1)
+    with pytest.raises(hta.MiSgemmError):
+        hta.mi_sgemm_get_plan(hta.KERNEL_MFMA, 99, 1, 1, 1)
+    with pytest.raises(hta.MiSgemmError):
+        hta.mi_sgemm_get_plan(hta.KERNEL_MFMA, -1, -1, 1, 1)
+
+
+# Fake, never-dereferenced device addresses: every call below must return an
+# error (or a no-op) before anything is enqueued.
+P = 0x10000
+
+
+@pytest.mark.parametrize("fn", [hta.mi_sgemm, hta.mi_sgemm_valu])
+def test_argument_errors(fn):
+    E = hta
+    assert fn(-1, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4) == E.ERROR_INVALID_VALUE
+    assert fn(4, -1, 4, 1.0, P, 4, P, 4, 0.0, P, 4) == E.ERROR_INVALID_VALUE
+    assert fn(4, 4, -1, 1.0, P, 4, P, 4, 0.0, P, 4) == E.ERROR_INVALID_VALUE
+    assert fn(4, 4, 8, 1.0, P, 7, P, 4, 0.0, P, 4) == E.ERROR_INVALID_LD
+    assert fn(4, 6, 8, 1.0, P, 8, P, 5, 0.0, P, 6) == E.ERROR_INVALID_LD
+    assert fn(4, 6, 8, 1.0, P, 8, P, 6, 0.0, P, 5) == E.ERROR_INVALID_LD
+    assert fn(4, 4, 4, 1.0, P, 4, P, 4, 0.0, None, 4) == E.ERROR_NULL_POINTER
+    assert fn(4, 4, 4, 1.0, None, 4, P, 4, 0.0, P, 4) == E.ERROR_NULL_POINTER
+    assert fn(4, 4, 4, 1.0, P, 4, None, 4, 0.0, P, 4) == E.ERROR_NULL_POINTER
+    # nothing to do: success without touching any pointer or device
+    assert fn(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4) == E.SUCCESS
+    assert fn(4, 0, 4, 1.0, None, 4, None, 1, 0.0, None, 1) == E.SUCCESS
+
+
+def test_splitk_argument_errors():
+    E, f = hta, hta.mi_sgemm_splitk
+    ws = hta.mi_sgemm_splitk_workspace_bytes(64, 64, 1024, 0)
+    assert f(64, 64, 1024, 1.0, P, 1024, P, 64, 0.0, P, 64, -1, P, ws) == E.ERROR_INVALID_VALUE
+    assert f(64, 64, 1024, 1.0, P, 1024, P, 64, 0.0, P, 64, 1025, P, ws) == E.ERROR_INVALID_VALUE
+    assert f(64, 64, 1024, 1.0, P, 1000, P, 64, 0.0, P, 64, 0, P, ws) == E.ERROR_INVALID_LD
+    assert f(64, 64, 1024, 1.0, P, 1024, P, 64, 0.0, P, 64, 0, P, ws - 1) == E.ERROR_WORKSPACE
+    assert f(64, 64, 1024, 1.0, P, 1024, P, 64, 0.0, P, 64, 0, None, ws) == E.ERROR_WORKSPACE
+    assert f(64, 64, 1024, 1.0, None, 1024, P, 64, 0.0, P, 64, 0, P, ws) == E.ERROR_NULL_POINTER
+    assert f(0, 64, 1024, 1.0, None, 1024, None, 64, 0.0, None, 64, 0, None, 0) == E.SUCCESS
+
+
+def test_with_config_rejects_unknown_ids():
+    n = hta.mi_sgemm_config_count(hta.KERNEL_MFMA)
+    assert n >= 1
+    r = hta.mi_sgemm_with_config(hta.KERNEL_MFMA, n, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    assert r == hta.ERROR_INVALID_VALUE
+    r = hta.mi_sgemm_with_config(hta.KERNEL_VALU, 1, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    assert r == hta.ERROR_INVALID_VALUE
+    r = hta.mi_sgemm_with_config(5, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    assert r == hta.ERROR_INVALID_VALUE
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; this checks the no-device path")
+    assert hta.mi_sgemm(4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4) == hta.ERROR_DEVICE

@@ -1,0 +1,281 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU
+oracle on the same seeded inputs.
+
+Bars: floating-point results within the tolerance in tests/parity.py; results
+on integer-valued operands bit-exact; padding of A and B (NaN) never read,
+padding of C (sentinel) never written.  At the full workload sizes the oracle
+computes sampled rows, and whole-matrix properties (row and column sums of an
+integer product, finiteness, untouched pads) cover every element.
+"""
+import numpy as np
+import pytest
+
+import synth
+from parity import assert_close, assert_exact
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import hpc_tiling_amd as hta
+    N_MFMA_CFG = hta.mi_sgemm_config_count(hta.KERNEL_MFMA)
+else:  # collected on a CPU host: every test here is skipped below
+    hta = None
+    N_MFMA_CFG = 6
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def upload(arr, cols):
+    t = torch.from_numpy(np.ascontiguousarray(arr)).to("cuda")
+    return t, t[:, :cols]
+
+
+def run_kernel(kind, A, B, C, alpha, beta):
+    """Launch one of the paths on tensor views; returns after synchronising."""
+    if kind == "mfma":
+        hta.sgemm(A, B, C, alpha, beta)
+    elif kind.startswith("mfma_cfg"):
+        hta.sgemm(A, B, C, alpha, beta, config=int(kind[len("mfma_cfg"):]))
+    elif kind == "valu":
+        hta.sgemm_valu(A, B, C, alpha, beta)
+    elif kind == "splitk":
+        hta.sgemm_splitk(A, B, C, alpha, beta, splits=0)
+    elif kind.startswith("splitk"):
+        hta.sgemm_splitk(A, B, C, alpha, beta, splits=int(kind[len("splitk"):]))
+    else:
+        raise ValueError(kind)
+    torch.cuda.synchronize()
+
+
+def gpu_gemm(kind, w, A, B, C):
+    """Run `kind` on padded host arrays; returns the full padded C back."""
+    Ad, Av = upload(A, w.k)
+    Bd, Bv = upload(B, w.n)
+    Cd, Cv = upload(C, w.n)
+    run_kernel(kind, Av, Bv, Cv, w.alpha, w.beta)
+    out = Cd.cpu().numpy()
+    del Ad, Bd, Cd
+    return out
+
+
+def check_pads(out, C_in, n, what):
+    assert np.array_equal(out[:, n:], C_in[:, n:]), f"{what}: C padding written"
+    assert np.all(np.isfinite(out[:, :n])), f"{what}: non-finite output (NaN pad read?)"
+
+
+def full_check(orc, kind, w, integer):
+    A, B, C = synth.operands(w, integer_twin=integer)
+    say(kind, w.name, "int" if integer else "float")
+    out = gpu_gemm(kind, w, A, B, C)
+    check_pads(out, C, w.n, kind)
+    ref = orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, want_g=True)
+    want = ref["C"].reshape(w.m, w.ldc)[:, :w.n]
+    got = out[:, :w.n]
+    if integer:
+        assert_exact(got, want, f"{kind} {w.name} int")
+    else:
+        assert_close(got, want, ref["G"], w.alpha, w.beta, C[:, :w.n], f"{kind} {w.name}")
+
+
+def sampled_check(orc, kind, w, integer, nrows, seed=0):
+    A, B, C = synth.operands(w, integer_twin=integer)
+    say(kind, w.name, "int" if integer else "float", f"rows={nrows}")
+    out = gpu_gemm(kind, w, A, B, C)
+    check_pads(out, C, w.n, kind)
+    rows = synth.sample_rows([w.wid, 99, seed], w.m, nrows)
+    ref = orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
+                    rows=rows, want_g=True)
+    want = ref["C"].reshape(w.m, w.ldc)[rows, :w.n]
+    got = out[rows, :w.n]
+    if integer:
+        assert_exact(got, want, f"{kind} {w.name} int rows")
+        # every element: row sums and column sums of alpha*A*B + beta*C (exact
+        # in float64 for these integer inputs)
+        Ai = A[:, :w.k].astype(np.float64)
+        Bi = B[:, :w.n].astype(np.float64)
+        Ci = C[:, :w.n].astype(np.float64)
+        full = out[:, :w.n].astype(np.float64)
+        beta_term = w.beta * Ci if w.beta != 0 else 0.0
+        row_want = w.alpha * (Ai @ Bi.sum(axis=1)) + (beta_term.sum(axis=1) if w.beta != 0 else 0.0)
+        col_want = w.alpha * (Ai.sum(axis=0) @ Bi) + (beta_term.sum(axis=0) if w.beta != 0 else 0.0)
+        assert np.array_equal(full.sum(axis=1), row_want), "row sums"
+        assert np.array_equal(full.sum(axis=0), col_want), "column sums"
+    else:
+        assert_close(got, want, ref["G"], w.alpha, w.beta, C[rows, :w.n], f"{kind} {w.name}")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Small ragged shapes on every path and every tile configuration
+# ---------------------------------------------------------------------------
+KINDS = (["mfma", "valu", "splitk", "splitk3", "splitk1"]
+         + [f"mfma_cfg{i}" for i in range(N_MFMA_CFG)])
+SHAPES = [(1, 1, 1), (7, 9, 5), (33, 65, 17), (130, 257, 300), (255, 129, 64), (64, 128, 2049)]
+
+
+@pytest.mark.parametrize("ld_pad", [0, 3], ids=["ld=w", "ld=w+3"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
+@pytest.mark.parametrize("kind", KINDS)
+def test_small_shapes(orc, kind, shape, ld_pad):
+    m, n, k = shape
+    base = synth.Workload(0, "small", m, n, k, k + ld_pad, n + ld_pad, n + ld_pad + 1,
+                          "uniform", None, 1.0, 0.0)
+    full_check(orc, kind, base, integer=False)
+    wi = base.scaled(dist_c="int3", alpha=1.5, beta=0.5)
+    full_check(orc, kind, wi, integer=True)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+def test_workload_256(orc, kind, integer):
+    full_check(orc, kind, synth.workload(0), integer)
+
+
+@pytest.mark.parametrize("kind", ["mfma", "valu"])
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+def test_workload_2048(orc, kind, integer):
+    sampled_check(orc, kind, synth.workload(1), integer, nrows=64)
+
+
+@pytest.mark.parametrize("kind", ["mfma", "valu"])
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+def test_workload_8192_alpha_beta(orc, kind, integer):
+    sampled_check(orc, kind, synth.workload(2), integer, nrows=12)
+
+
+@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+def test_workload_tails(orc, kind, integer):
+    sampled_check(orc, kind, synth.workload(3), integer, nrows=48)
+
+
+@pytest.mark.parametrize("kind", ["splitk", "mfma"])
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+def test_workload_splitk(orc, kind, integer):
+    sampled_check(orc, kind, synth.workload(4), integer, nrows=6)
+
+
+# ---------------------------------------------------------------------------
+# Special cases of the interface
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
+def test_beta_zero_ignores_nan_c(kind):
+    say("beta0 nan C", kind)
+    m, n, k = 70, 90, 33
+    A = torch.ones((m, k), device="cuda")
+    B = torch.ones((k, n), device="cuda")
+    C = torch.full((m, n), float("nan"), device="cuda")
+    run_kernel(kind, A, B, C, 2.0, 0.0)
+    assert torch.equal(C, torch.full((m, n), 2.0 * k, device="cuda"))
+
+
+@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
+def test_alpha_zero_and_k_zero(kind):
+    say("alpha0/k0", kind)
+    m, n = 45, 77
+    g = torch.Generator(device="cpu").manual_seed(1)
+    Cin = torch.randn((m, n), generator=g)
+    A = torch.full((m, 8), float("nan"), device="cuda")
+    B = torch.full((8, n), float("inf"), device="cuda")
+    C = Cin.to("cuda")
+    run_kernel(kind, A, B, C, 0.0, 0.75)
+    want = (Cin.double() * 0.75).float()
+    assert torch.equal(C.cpu(), want)
+    C = Cin.to("cuda")
+    run_kernel(kind, A[:, :0], B[:0, :], C, 1.0, -1.25)
+    assert torch.equal(C.cpu(), (Cin.double() * -1.25).float())
+    C = Cin.to("cuda")
+    run_kernel(kind, A[:, :0], B[:0, :], C, 1.0, 0.0)
+    assert torch.equal(C.cpu(), torch.zeros((m, n)))
+
+
+@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
+def test_misaligned_operands(orc, kind):
+    """Pointers one float off 16-byte alignment take the element-load path."""
+    say("misaligned", kind)
+    m, n, k = 97, 131, 203
+    rng = np.random.default_rng(5)
+    Ah = rng.integers(-3, 4, (m, k + 1)).astype(np.float32)
+    Bh = rng.integers(-3, 4, (k, n + 1)).astype(np.float32)
+    Ad = torch.from_numpy(Ah).cuda()
+    Bd = torch.from_numpy(Bh).cuda()
+    Cbig = torch.zeros((m * n + 1,), device="cuda")
+    C = Cbig[1:].view(m, n)
+    run_kernel(kind, Ad[:, 1:], Bd[:, 1:], C, 1.0, 0.0)
+    want = (Ah[:, 1:].astype(np.int64) @ Bh[:, 1:].astype(np.int64)).astype(np.float32)
+    assert_exact(C.cpu().numpy(), want, "misaligned")
+
+
+@pytest.mark.parametrize("kind", ["mfma", "splitk"])
+def test_deterministic(kind):
+    say("determinism", kind)
+    w = synth.workload(1)
+    A, B, _ = synth.operands(w)
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C1 = torch.empty((w.m, w.n), device="cuda")
+    C2 = torch.empty((w.m, w.n), device="cuda")
+    run_kernel(kind, Ad, Bd, C1, 1.0, 0.0)
+    run_kernel(kind, Ad, Bd, C2, 1.0, 0.0)
+    assert torch.equal(C1, C2)
+
+
+def test_splitk_matches_unsplit(orc):
+    say("splitk vs unsplit")
+    w = synth.workload(3)
+    A, B, C = synth.operands(w)
+    out_s = gpu_gemm("splitk", w, A, B, C)
+    out_u = gpu_gemm("mfma", w, A, B, C)
+    rows = synth.sample_rows([3, 7], w.m, 8)
+    ref = orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
+                    rows=rows, want_g=True)
+    # both within tolerance of the oracle, and of each other (twice the bar)
+    G = ref["G"]
+    assert_close(out_s[rows, :w.n], out_u[rows, :w.n], 2 * G, 1.0, 0.0, 0.0, "split vs unsplit")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 5, 7, 64])
+def test_splitk_combine_partial_waves(splits):
+    """Output counts that leave the last wave of the combine partly empty
+    (m*n not a multiple of 64, nor of 4), split counts that are not multiples
+    of the four lane groups: exact on integer operands."""
+    say("combine", splits)
+    rng = np.random.default_rng(splits)
+    for (m, n, k) in [(7, 9, 640), (1, 3, 512), (13, 5, 1000)]:
+        Ah = rng.integers(-3, 4, (m, k)).astype(np.float32)
+        Bh = rng.integers(-3, 4, (k, n)).astype(np.float32)
+        C = torch.zeros((m, n), device="cuda")
+        s = min(splits, k)
+        hta.sgemm_splitk(torch.from_numpy(Ah).cuda(), torch.from_numpy(Bh).cuda(), C,
+                         1.0, 0.0, splits=s)
+        torch.cuda.synchronize()
+        want = (Ah.astype(np.int64) @ Bh.astype(np.int64)).astype(np.float32)
+        assert_exact(C.cpu().numpy(), want, f"combine {m}x{n}x{k} s={s}")
+
+
+def test_non_default_stream():
+    say("stream")
+    s = torch.cuda.Stream()
+    m, n, k = 300, 200, 100
+    A = torch.ones((m, k), device="cuda")
+    B = torch.ones((k, n), device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        C = torch.empty((m, n), device="cuda")
+        hta.sgemm(A, B, C, 1.0, 0.0)
+        D = torch.empty((m, n), device="cuda")
+        hta.sgemm_splitk(A, B, D, 1.0, 0.0, splits=4)
+    s.synchronize()
+    assert torch.equal(C, torch.full((m, n), float(k), device="cuda"))
+    assert torch.equal(D, torch.full((m, n), float(k), device="cuda"))
