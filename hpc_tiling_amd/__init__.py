@@ -8,7 +8,7 @@ torch tensors to them.  Every step of the computation runs in the library's
 HIP kernels; there is no fallback path.  Importing raises ImportError when the
 library has not been built (``python hpc_tiling_amd/build.py``).
 
-torch is used for device memory and streams only, and is imported lazily.
+torch is used for device memory and streams only.
 """
 from __future__ import annotations
 
@@ -46,6 +46,15 @@ if not LIB_PATH.exists():
     raise ImportError(
         f"{LIB_PATH} is missing: build it with `python hpc_tiling_amd/build.py` "
         "(the HIP library is required; there is no other implementation)")
+
+# torch bundles its own HIP runtime under the same SONAME (libamdhip64.so.7).
+# Loading torch first makes the library bind to that runtime instead of
+# pulling a second copy into the process (device pointers and streams are only
+# valid in the runtime that created them).
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # pragma: no cover - C callers without torch
+    _torch = None
 
 lib = ctypes.CDLL(str(LIB_PATH))
 

@@ -50,7 +50,9 @@ def run_kernel(kind, A, B, C, alpha, beta):
     elif kind == "splitk":
         hta.sgemm_splitk(A, B, C, alpha, beta, splits=0)
     elif kind.startswith("splitk"):
-        hta.sgemm_splitk(A, B, C, alpha, beta, splits=int(kind[len("splitk"):]))
+        # a split count above k is an argument error; ask for at most k slices
+        splits = min(int(kind[len("splitk"):]), A.shape[1])
+        hta.sgemm_splitk(A, B, C, alpha, beta, splits=splits)
     else:
         raise ValueError(kind)
     torch.cuda.synchronize()
