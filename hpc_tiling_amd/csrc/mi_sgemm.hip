@@ -35,20 +35,17 @@ constexpr MfmaConfig make_cfg(bool with_split) {
                       with_split ? &sgemm_mfma_kernel<T, false, true> : nullptr};
 }
 
-using Cfg128x128x16 = MfmaTile<128, 128, 16, 2, 2>;
-using Cfg128x128x32 = MfmaTile<128, 128, 32, 2, 2>;
-using Cfg128x64x32 = MfmaTile<128, 64, 32, 2, 2>;
-using Cfg256x128x16 = MfmaTile<256, 128, 16, 2, 2>;
-using Cfg128x128x16w8 = MfmaTile<128, 128, 16, 2, 4>;
-using Cfg64x64x32 = MfmaTile<64, 64, 32, 2, 2>;
-
+// MfmaTile<BM, BN, BK, waves along m, waves along n>
 const MfmaConfig kMfmaConfigs[] = {
-    make_cfg<Cfg128x128x16>(true),     // 0
-    make_cfg<Cfg128x128x32>(true),     // 1
-    make_cfg<Cfg128x64x32>(false),     // 2
-    make_cfg<Cfg256x128x16>(false),    // 3
-    make_cfg<Cfg128x128x16w8>(false),  // 4
-    make_cfg<Cfg64x64x32>(false),      // 5
+    make_cfg<MfmaTile<128, 128, 16, 2, 2>>(true),   // 0
+    make_cfg<MfmaTile<128, 128, 32, 2, 2>>(false),  // 1
+    make_cfg<MfmaTile<128, 128, 16, 2, 4>>(false),  // 2
+    make_cfg<MfmaTile<128, 128, 32, 2, 4>>(false),  // 3
+    make_cfg<MfmaTile<256, 128, 16, 2, 4>>(false),  // 4
+    make_cfg<MfmaTile<128, 256, 16, 2, 4>>(false),  // 5
+    make_cfg<MfmaTile<64, 64, 32, 2, 2>>(false),    // 6
+    make_cfg<MfmaTile<256, 128, 32, 2, 4>>(false),  // 7
+    make_cfg<MfmaTile<128, 64, 32, 2, 2>>(false),   // 8
 };
 constexpr int kNumMfmaConfigs = sizeof(kMfmaConfigs) / sizeof(kMfmaConfigs[0]);
 constexpr int kSplitConfig = 0;  // tile configuration of the split-K partial kernel

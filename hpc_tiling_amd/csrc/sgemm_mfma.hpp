@@ -4,17 +4,16 @@
 // 基于 register 计算 and prefetch 和双缓冲, re-planned for gfx950):
 //   * a workgroup of WGM x WGN waves owns a BM x BN tile of C and walks k in
 //     steps of BK ("big iterations");
-//   * each step stages a BM x BK tile of A and a BK x BN tile of B from HBM
-//     through VGPRs into one of two LDS buffers with 16-byte loads whose
-//     adjacent lanes read adjacent addresses (page aerisun.top, sections on
-//     coalescing and float4); out-of-range elements are stored as zeros
-//     (page aerisun.top, section "Shared Tiling 与 block 内复用");
+//   * each step stages a BM x BK tile of A and a BK x BN tile of B in one of
+//     three LDS buffers.  Interior tiles use gfx950's direct global->LDS loads
+//     (buffer_load_dwordx4 ... lds: 16 bytes per lane, no VGPRs involved), issued
+//     two steps ahead; tiles on the m/n edge, the partial last k step and
+//     unaligned operands use 16-byte (or element) loads through VGPRs with
+//     out-of-range elements stored as zeros (page aerisun.top, section
+//     "Shared Tiling 与 block 内复用");
 //   * each wave owns a (BM/WGM) x (BN/WGN) sub-tile held as 32 x 32 blocks
 //     of v_mfma_f32_32x32x2_f32 accumulators and reads its A and B fragments
-//     from LDS;
-//   * the global loads of step t+1 are issued before the MFMAs of step t and
-//     written to the other LDS buffer after them, so one barrier per step
-//     suffices.
+//     from LDS one group of 8 k ahead of the MFMAs that use them.
 //
 // k ordering inside a step.  One 16-byte LDS read gives lane (i, h)
 // (i = lane % 32, h = lane / 32) the four A values A[i][8g+4h .. 8g+4h+3] of a
@@ -23,12 +22,19 @@
 // k = 8g+s and 8g+4+s, so the four MFMAs cover the eight k values of the
 // group exactly once with matching A and B indices.
 //
-// LDS layout.  A: BM rows of BK (+4 pad) floats (m-major, as in memory); with
-// the pad, the 16-byte fragment reads of 16 consecutive rows fall on
-// disjoint bank quads.  B: BK rows of BN (+8 pad) floats (k-major, as in
-// memory); the pad puts rows k and k+4 (read by the two lane halves) half a
-// bank cycle apart.
+// LDS layout (64 banks of 4 bytes; a direct load writes 64 lanes x 16 bytes
+// to 1 KiB of consecutive LDS, so tiles are unpadded and XOR-swizzled in
+// 16-byte chunks instead):
+//   * A: BM rows of BK floats (m-major, as in memory); logical chunk c of row
+//     r sits at chunk c ^ swz(r), swz(r) = (r * CA / 16) % CA with CA = BK / 4
+//     chunks per row.  The 16 lanes of a fragment read (16 consecutive rows,
+//     same logical chunk) then cover all 16 bank quads.
+//   * B: BK rows of BN floats (k-major, as in memory); rows with bit 2 set
+//     swap the two 32-float halves of every 64 floats.  The lane halves of a
+//     fragment read take rows k and k+4, which then fall on disjoint banks.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -37,30 +43,84 @@ namespace mi {
 template <int BM_, int BN_, int BK_, int WGM_, int WGN_>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
+    static constexpr int STAGES = 3;                      // LDS buffers in the ring
     static constexpr int WAVES = WGM * WGN;
     static constexpr int NT = 64 * WAVES;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // per-wave tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 blocks per wave
-    static constexpr int LDA_S = BK + 4;                  // LDS row stride of A
-    static constexpr int LDB_S = BN + 8;                  // LDS row stride of B
-    static constexpr int A_Q = BK / 4;                    // float4 per A row
-    static constexpr int B_Q = BN / 4;                    // float4 per B row
-    static constexpr int A_PER = BM * BK / 4 / NT;        // A float4 per thread
-    static constexpr int B_PER = BK * BN / 4 / NT;        // B float4 per thread
-    static constexpr int LDS_BYTES = 2 * (BM * LDA_S + BK * LDB_S) * 4;
-    static_assert(BK % 8 == 0, "k step must hold whole groups of 8");
+    static constexpr int GROUPS = BK / 8;                 // groups of 8 k per step
+    static constexpr int CA = BK / 4;                     // 16-byte chunks per A row
+    static constexpr int CB = BN / 4;                     // 16-byte chunks per B row
+    static constexpr int A_PER = BM * CA / NT;            // A chunks per thread per step
+    static constexpr int B_PER = BK * CB / NT;            // B chunks per thread per step
+    static constexpr int LDS_BYTES = STAGES * (BM * BK + BK * BN) * 4;
+    static_assert(BK == 16 || BK == 32, "A swizzle assumes 4 or 8 chunks per row");
+    static_assert(BN % 64 == 0, "B swizzle swaps 32-float halves of 64-float blocks");
+    static_assert(GROUPS % 2 == 0, "fragment double-buffering needs an even group count");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BM * BK / 4 % NT == 0 && BK * BN / 4 % NT == 0, "load slots must divide evenly");
+    static_assert(BM * CA % NT == 0 && BK * CB % NT == 0, "load slots must divide evenly");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
+
+    __device__ static constexpr int a_swz(int row) { return (row * CA / 16) % CA; }
+    __device__ static constexpr int b_swz(int krow) { return 8 * ((krow >> 2) & 1); }
 };
+
+// Word 3 of a raw (untyped) buffer resource on gfx9-class parts: 32-bit data
+// format, no swizzling; with stride 0 the range check is a byte count.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(float *p) {
+    return (__attribute__((address_space(3))) void *)p;
+}
+
+// One buffer_load_dwordx4 ... lds: 16 bytes from base + voffset (per lane)
+// into LDS at lds + 16 * lane.  The resource covers 2^31 - 1 bytes from base.
+// (Kept out of the kernel template: the host compilation pass drops the
+// launch stub of a kernel whose body builds a buffer resource.)
+__device__ __forceinline__ void load_lds16(const float *base, float *lds, int voffset) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, 0x7fffffff,
+                                                        kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds), 16, voffset, 0, 0, 0);
+}
 
 // SPLIT: workgroup (tile, slice) sums k in [slice*k_per_split, ...) into the
 // raw partial ws[slice] (no alpha/beta); otherwise the full k range is summed
 // and C = alpha*acc + beta*C is written.  VEC: A and B allow 16-byte loads.
+//
+// Pipeline (one barrier per step, buffers used round-robin):
+//   top of step t    issue the tile of step t+2 into buffer (t+2) % 3 (direct
+//                    loads, or VGPR loads for the masked cases)
+//   body             MFMAs of step t on buffer t % 3; the last group also reads
+//                    the first fragments of step t+1 from buffer (t+1) % 3
+//   end of step t    (VGPR case) write the staged tile; barrier
+// Buffer (t+2) % 3 was last read during step t-1, before the barrier that
+// ended it; buffer (t+1) % 3 was filled during step t-1 and completed by the
+// same barrier (which waits for the direct loads), so the first fragments of
+// step t+1 can be read before the barrier of step t and the MFMA stream does
+// not wait for LDS at a step boundary.
 template <class T, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) float As[2][T::BM * T::LDA_S];
-    __shared__ __attribute__((aligned(16))) float Bs[2][T::BK * T::LDB_S];
+    // One LDS object per ring stage, always indexed at compile time: the
+    // compiler can then tell the buffer a direct load writes from the buffers
+    // being read, and does not hold the MFMAs back until the load lands.
+    __shared__ __attribute__((aligned(1024))) float As0[T::BM * T::BK];
+    __shared__ __attribute__((aligned(1024))) float As1[T::BM * T::BK];
+    __shared__ __attribute__((aligned(1024))) float As2[T::BM * T::BK];
+    __shared__ __attribute__((aligned(1024))) float Bs0[T::BK * T::BN];
+    __shared__ __attribute__((aligned(1024))) float Bs1[T::BK * T::BN];
+    __shared__ __attribute__((aligned(1024))) float Bs2[T::BK * T::BN];
+    auto a_buf = [&](auto s) -> float * {
+        constexpr int S = decltype(s)::value;
+        if constexpr (S == 0) return As0;
+        else if constexpr (S == 1) return As1;
+        else return As2;
+    };
+    auto b_buf = [&](auto s) -> float * {
+        constexpr int S = decltype(s)::value;
+        if constexpr (S == 0) return Bs0;
+        else if constexpr (S == 1) return Bs1;
+        else return Bs2;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -83,56 +143,89 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     const int nsteps = (kend - kbeg + T::BK - 1) / T::BK;
     const bool full_m = m0 + T::BM <= p.m;
     const bool full_n = n0 + T::BN <= p.n;
+    // Steps whose tiles are complete and aligned are loaded directly into LDS
+    // (byte offsets inside one tile step must fit the 31-bit buffer offset).
+    const bool direct_ok = VEC && full_m && full_n &&
+                           p.lda < (1LL << 31) / (4LL * T::BM) && p.ldb < (1LL << 31) / (4LL * T::BK);
+    const int ndirect = direct_ok ? (kend - kbeg) / T::BK : 0;
 
-    // ---- global -> VGPR staging ------------------------------------------
-    f32x4 ra[T::A_PER], rb[T::B_PER];
     const float *Ablk = p.A + (long long)m0 * p.lda;
     const float *Bblk = p.B + n0;
 
-    auto load_step = [&](int step) {
-        const int k0 = kbeg + step * T::BK;
-        const bool full_k = k0 + T::BK <= kend;
-#pragma unroll
-        for (int i = 0; i < T::A_PER; ++i) {
-            const int s = tid + i * T::NT;
-            const int r = s / T::A_Q, c = 4 * (s % T::A_Q);
-            const float *src = Ablk + (long long)r * p.lda + k0 + c;
-            if (VEC && full_m && full_k) {
-                ra[i] = *reinterpret_cast<const f32x4 *>(src);
-            } else {
-                const int valid = (m0 + r < p.m) ? min(4, kend - (k0 + c)) : 0;
-                ra[i] = load4_masked<VEC>(src, valid);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < T::B_PER; ++i) {
-            const int s = tid + i * T::NT;
-            const int r = s / T::B_Q, c = 4 * (s % T::B_Q);
-            const float *src = Bblk + (long long)(k0 + r) * p.ldb + c;
-            if (VEC && full_n && full_k) {
-                rb[i] = *reinterpret_cast<const f32x4 *>(src);
-            } else {
-                const int valid = (k0 + r < kend) ? min(4, p.n - (n0 + c)) : 0;
-                rb[i] = load4_masked<VEC>(src, valid);
-            }
-        }
+    // Chunk q = tid + i * NT of a tile (the chunk lane `lane` of wave `wave`
+    // writes in the i-th load instruction): its row and logical chunk.
+    auto a_chunk = [&](int i, int &row, int &c) {
+        const int q = tid + i * T::NT;
+        row = q / T::CA;
+        c = (q % T::CA) ^ T::a_swz(row);
     };
-    auto store_step = [&](int buf) {
+    auto b_chunk = [&](int i, int &row, int &c) {
+        const int q = tid + i * T::NT;
+        row = q / T::CB;
+        c = (q % T::CB) ^ T::b_swz(row);
+    };
+
+    // ---- direct global -> LDS loads (complete, aligned tiles) ---------------
+    // buffer_load_dwordx4 ... lds through a per-step buffer resource whose
+    // base is the step's first element; each lane supplies a byte offset.
+    // (The MUBUF form rather than global_load_lds: the compiler treats a FLAT
+    // access that may touch LDS as unordered and would then wait for every
+    // outstanding LDS read before each MFMA group.)
+    auto load_direct = [&](int step, auto buf) {
+        float *as = a_buf(buf), *bs = b_buf(buf);
+        const int k0 = kbeg + step * T::BK;
+        const float *abase = Ablk + k0;
+        const float *bbase = Bblk + (long long)k0 * p.ldb;
 #pragma unroll
         for (int i = 0; i < T::A_PER; ++i) {
-            const int s = tid + i * T::NT;
-            const int r = s / T::A_Q, c = 4 * (s % T::A_Q);
-            *reinterpret_cast<f32x4 *>(&As[buf][r * T::LDA_S + c]) = ra[i];
+            int row, c;
+            a_chunk(i, row, c);
+            load_lds16(abase, as + (i * T::WAVES + wave) * 256,
+                       (int)(4 * ((long long)row * p.lda + 4 * c)));
         }
 #pragma unroll
         for (int i = 0; i < T::B_PER; ++i) {
-            const int s = tid + i * T::NT;
-            const int r = s / T::B_Q, c = 4 * (s % T::B_Q);
-            *reinterpret_cast<f32x4 *>(&Bs[buf][r * T::LDB_S + c]) = rb[i];
+            int row, c;
+            b_chunk(i, row, c);
+            load_lds16(bbase, bs + (i * T::WAVES + wave) * 256,
+                       (int)(4 * ((long long)row * p.ldb + 4 * c)));
         }
     };
 
-    // ---- accumulators -----------------------------------------------------
+    // ---- masked loads through VGPRs (edges, k tail, unaligned) -------------
+    struct Stage {
+        f32x4 a[T::A_PER], b[T::B_PER];
+    };
+    auto load_regs = [&](Stage &st, int step) {
+        const int k0 = kbeg + step * T::BK;
+#pragma unroll
+        for (int i = 0; i < T::A_PER; ++i) {
+            int row, c;
+            a_chunk(i, row, c);
+            const float *src = Ablk + (long long)row * p.lda + k0 + 4 * c;
+            const int valid = (m0 + row < p.m) ? min(4, kend - (k0 + 4 * c)) : 0;
+            st.a[i] = load4_masked<VEC>(src, valid);
+        }
+#pragma unroll
+        for (int i = 0; i < T::B_PER; ++i) {
+            int row, c;
+            b_chunk(i, row, c);
+            const float *src = Bblk + (long long)(k0 + row) * p.ldb + 4 * c;
+            const int valid = (k0 + row < kend) ? min(4, p.n - (n0 + 4 * c)) : 0;
+            st.b[i] = load4_masked<VEC>(src, valid);
+        }
+    };
+    auto store_regs = [&](const Stage &st, auto buf) {
+        float *as = a_buf(buf), *bs = b_buf(buf);
+#pragma unroll
+        for (int i = 0; i < T::A_PER; ++i)
+            *reinterpret_cast<f32x4 *>(as + 4 * (tid + i * T::NT)) = st.a[i];
+#pragma unroll
+        for (int i = 0; i < T::B_PER; ++i)
+            *reinterpret_cast<f32x4 *>(bs + 4 * (tid + i * T::NT)) = st.b[i];
+    };
+
+    // ---- accumulators and fragments ----------------------------------------
     f32x16 acc[T::FM][T::FN];
 #pragma unroll
     for (int a = 0; a < T::FM; ++a)
@@ -142,43 +235,106 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
     const int li = lane & 31, lh = lane >> 5;
-    const int a_off = (wm * T::WTM + li) * T::LDA_S + 4 * lh;
-    const int b_off = 4 * lh * T::LDB_S + wn * T::WTN + li;
-
-    if (nsteps > 0) {
-        load_step(0);
-        store_step(0);
-        __syncthreads();
-    }
-    for (int step = 0; step < nsteps; ++step) {
-        const int buf = step & 1;
-        const bool more = step + 1 < nsteps;
-        if (more) load_step(step + 1);
-
-        const float *as = &As[buf][a_off];
-        const float *bs = &Bs[buf][b_off];
+    int a_row_off[T::FM], a_swz[T::FM], b_col[T::FN];
 #pragma unroll
-        for (int g = 0; g < T::BK / 8; ++g) {
-            f32x4 af[T::FM];
-            float bf[T::FN][4];
+    for (int a = 0; a < T::FM; ++a) {
+        const int row = wm * T::WTM + 32 * a + li;
+        a_row_off[a] = row * T::BK;
+        a_swz[a] = T::a_swz(row);
+    }
+#pragma unroll
+    for (int b = 0; b < T::FN; ++b)
+        b_col[b] = ((wn * T::WTN + 32 * b + li) ^ (32 * lh)) + 4 * lh * T::BN;
+
+    struct Frag {
+        f32x4 a[T::FM];
+        float b[T::FN][4];
+    };
+    auto read_frag = [&](Frag &f, auto buf, int g) {
+        const float *as = a_buf(buf), *bs = b_buf(buf);
+#pragma unroll
+        for (int a = 0; a < T::FM; ++a)
+            f.a[a] = *reinterpret_cast<const f32x4 *>(
+                as + a_row_off[a] + 4 * ((2 * g + lh) ^ a_swz[a]));
+#pragma unroll
+        for (int b = 0; b < T::FN; ++b)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) f.b[b][s] = bs[b_col[b] + (8 * g + s) * T::BN];
+    };
+    auto mfma_group = [&](const Frag &f) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int a = 0; a < T::FM; ++a)
-                af[a] = *reinterpret_cast<const f32x4 *>(as + a * 32 * T::LDA_S + 8 * g);
 #pragma unroll
-            for (int b = 0; b < T::FN; ++b)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) bf[b][s] = bs[(8 * g + s) * T::LDB_S + 32 * b];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int a = 0; a < T::FM; ++a)
-#pragma unroll
-                    for (int b = 0; b < T::FN; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a][s], bf[b][s],
-                                                                         acc[a][b], 0, 0, 0);
-        }
-        if (more) store_step(buf ^ 1);
+                for (int b = 0; b < T::FN; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[a][s], f.b[b][s],
+                                                                     acc[a][b], 0, 0, 0);
+    };
+
+    // ---- main loop -----------------------------------------------------------
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if (nsteps > 0) {
+        Frag f[2];
+        // make the tiles of steps 0 and 1 resident
+        auto fill = [&](int step, auto buf) {
+            if (step < ndirect) {
+                load_direct(step, buf);
+            } else {
+                Stage st;
+                load_regs(st, step);
+                store_regs(st, buf);
+            }
+        };
+        fill(0, S0{});
+        if (nsteps > 1) fill(1, S1{});
         __syncthreads();
+        read_frag(f[0], S0{}, 0);
+
+        // One step with its ring position CUR = step % 3 fixed at compile time.
+        // DIRECT: the tile two steps ahead is loaded directly (the steady
+        // state of interior tiles -- no VGPR loads in that loop, so the
+        // compiler's wait counts never hold back the MFMAs); otherwise it goes
+        // through VGPRs (edge tiles, unaligned operands, the last k steps).
+        auto one_step = [&](int step, auto direct_tag, auto cur) {
+            constexpr bool DIRECT = decltype(direct_tag)::value;
+            constexpr int CUR = decltype(cur)::value;
+            using NXT = std::integral_constant<int, (CUR + 1) % 3>;  // (step + 1) % 3
+            using WRT = std::integral_constant<int, (CUR + 2) % 3>;  // (step + 2) % 3
+            const bool ahead = step + 2 < nsteps;
+            Stage st;
+            if (DIRECT)
+                load_direct(step + 2, WRT{});
+            else if (ahead)
+                load_regs(st, step + 2);
+            // The fences keep the scheduler from sinking the loads and the
+            // next group's LDS reads below the MFMAs that hide them.
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < T::GROUPS; ++g) {
+                if (g + 1 < T::GROUPS) {
+                    read_frag(f[(g + 1) & 1], cur, g + 1);
+                } else if (DIRECT || step + 1 < nsteps) {
+                    read_frag(f[0], NXT{}, 0);  // GROUPS is even: step+1 starts on set 0
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_group(f[g & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (!DIRECT && ahead) store_regs(st, WRT{});
+            __syncthreads();
+        };
+        auto dispatch = [&](int step, auto direct_tag) {
+            switch (step % 3) {
+                case 0: one_step(step, direct_tag, S0{}); break;
+                case 1: one_step(step, direct_tag, S1{}); break;
+                default: one_step(step, direct_tag, std::integral_constant<int, 2>{}); break;
+            }
+        };
+        int step = 0;
+        for (; step + 2 < ndirect; ++step) dispatch(step, std::true_type{});
+        for (; step < nsteps; ++step) dispatch(step, std::false_type{});
     }
 
     // ---- epilogue -----------------------------------------------------------
