@@ -63,7 +63,7 @@ def read_traffic(kernel: str, workload: str):
 
 
 def sclk_mhz():
-    """Current shader clock from sysfs, when readable."""
+    """Current shader clock from sysfs (the level marked '*'), when readable."""
     import glob
     for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
         try:
@@ -73,6 +73,38 @@ def sclk_mhz():
         except (OSError, ValueError, IndexError):
             continue
     return None
+
+
+class ClockSampler:
+    """Polls the shader clock from a host thread while the GPU works."""
+
+    def __init__(self, period_s=0.002):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = sclk_mhz()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"samples": len(v), "min": v[0], "median": v[len(v) // 2], "max": v[-1]}
 
 
 def make_step(kind, w, Av, Bv, Cv, ws):
@@ -185,8 +217,8 @@ def secondary(kinds_workloads, reps=10):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--kernel", default="mfma", help="mfma | valu | splitk | mfma_cfgN")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the oracle leg")
@@ -225,10 +257,9 @@ def main(argv=None):
     kind = args.kernel
     print(f"[bench] {kind} {w.name}: generating operands", file=sys.stderr, flush=True)
     host, dev, step = setup(w, kind)
-    sclk_before = sclk_mhz()
     print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
-    dt = time_steps(step, args.steps, args.warmup)
-    sclk_after = sclk_mhz()
+    with ClockSampler() as clocks:
+        dt = time_steps(step, args.steps, args.warmup)
     ms = 1e3 * dt / args.steps
     value = pm.tflops(w.m, w.n, w.k, dt, reps=args.steps)
 
@@ -265,7 +296,7 @@ def main(argv=None):
                    "ldc": w.ldc, "alpha": w.alpha, "beta": w.beta, "kernel": kind,
                    "layout": "row-major"},
         "frac_of_fp32_peak": value * 1e12 / pm.PEAK_FP32_MFMA,
-        "sclk_mhz": {"before": sclk_before, "after": sclk_after},
+        "sclk_mhz": clocks.summary(),
         "roofline": roof,
     }
     del dev, step

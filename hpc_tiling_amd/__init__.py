@@ -19,6 +19,7 @@ __all__ = [
     "LIB_PATH", "lib", "MiSgemmError", "Plan",
     "mi_sgemm", "mi_sgemm_valu", "mi_sgemm_splitk", "mi_sgemm_splitk_workspace_bytes",
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
+    "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
     "sgemm", "sgemm_valu", "sgemm_splitk", "splitk_workspace",
     "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "EXPORTED_SYMBOLS",
 ]
@@ -40,6 +41,7 @@ KERNEL_SPLITK = 2
 EXPORTED_SYMBOLS = (
     "mi_sgemm", "mi_sgemm_valu", "mi_sgemm_splitk_workspace_bytes", "mi_sgemm_splitk",
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
+    "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
 )
 
 if not LIB_PATH.exists():
@@ -90,6 +92,10 @@ lib.mi_sgemm_splitk_workspace_bytes.argtypes = [_i, _i, _i, _i]
 lib.mi_sgemm_splitk_workspace_bytes.restype = _sz
 lib.mi_sgemm_splitk.argtypes = _GEMM_ARGS + [_i, _vp, _sz, _vp]
 lib.mi_sgemm_splitk.restype = _i
+lib.mi_sgemm_splitk_with_config.argtypes = [_i] + _GEMM_ARGS + [_i, _vp, _sz, _vp]
+lib.mi_sgemm_splitk_with_config.restype = _i
+lib.mi_sgemm_splitk_with_config_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+lib.mi_sgemm_splitk_with_config_workspace_bytes.restype = _sz
 lib.mi_status_string.argtypes = [_i]
 lib.mi_status_string.restype = ctypes.c_char_p
 lib.mi_sgemm_get_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(Plan)]
@@ -129,6 +135,16 @@ def mi_sgemm_splitk(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws, ws
                     stream=None) -> int:
     return lib.mi_sgemm_splitk(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws,
                                ws_bytes, stream)
+
+
+def mi_sgemm_splitk_with_config(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                                ws, ws_bytes, stream=None) -> int:
+    return lib.mi_sgemm_splitk_with_config(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                                           splits, ws, ws_bytes, stream)
+
+
+def mi_sgemm_splitk_with_config_workspace_bytes(config, m, n, k, splits=0) -> int:
+    return lib.mi_sgemm_splitk_with_config_workspace_bytes(config, m, n, k, splits)
 
 
 def mi_status_string(status: int) -> str:
@@ -216,23 +232,33 @@ def sgemm_valu(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
     return C
 
 
-def splitk_workspace(m, n, k, splits=0, device="cuda"):
-    """A device workspace tensor large enough for mi_sgemm_splitk."""
+def splitk_workspace(m, n, k, splits=0, device="cuda", config=None):
+    """A device workspace tensor large enough for mi_sgemm_splitk (or, with
+    `config`, for mi_sgemm_splitk_with_config)."""
     import torch
-    nbytes = mi_sgemm_splitk_workspace_bytes(m, n, k, splits)
+    if config is None:
+        nbytes = mi_sgemm_splitk_workspace_bytes(m, n, k, splits)
+    else:
+        nbytes = mi_sgemm_splitk_with_config_workspace_bytes(config, m, n, k, splits)
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, stream=None):
+def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, stream=None,
+                 config=None):
     """Same as sgemm with the k range split into slices; `workspace` is a
     device tensor of at least mi_sgemm_splitk_workspace_bytes bytes (allocated
-    here when None)."""
+    here when None).  `config` forces the partial kernel's tile configuration."""
     m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
     if workspace is None:
-        workspace = splitk_workspace(m, n, k, splits, device=A.device)
+        workspace = splitk_workspace(m, n, k, splits, device=A.device, config=config)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.mi_sgemm_splitk(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
-                             workspace.data_ptr(), ws_bytes, _stream(stream))
+    if config is None:
+        st = lib.mi_sgemm_splitk(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
+                                 workspace.data_ptr(), ws_bytes, _stream(stream))
+    else:
+        st = lib.mi_sgemm_splitk_with_config(config, m, n, k, alpha, pa, lda, pb, ldb, beta, pc,
+                                             ldc, splits, workspace.data_ptr(), ws_bytes,
+                                             _stream(stream))
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_splitk")
     return C

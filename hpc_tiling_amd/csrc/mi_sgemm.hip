@@ -24,37 +24,59 @@ using KernelFn = void (*)(GemmArgs);
 struct MfmaConfig {
     int bm, bn, bk, wgm, wgn;
     KernelFn vec, scalar;              // full-k kernels
-    KernelFn split_vec, split_scalar;  // split-K partial kernels (may be null)
+    KernelFn split_vec, split_scalar;  // split-K partial kernels
 };
 
 template <class T>
-constexpr MfmaConfig make_cfg(bool with_split) {
+constexpr MfmaConfig make_cfg() {
     return MfmaConfig{T::BM, T::BN, T::BK, T::WGM, T::WGN,
                       &sgemm_mfma_kernel<T, true, false>, &sgemm_mfma_kernel<T, false, false>,
-                      with_split ? &sgemm_mfma_kernel<T, true, true> : nullptr,
-                      with_split ? &sgemm_mfma_kernel<T, false, true> : nullptr};
+                      &sgemm_mfma_kernel<T, true, true>, &sgemm_mfma_kernel<T, false, true>};
 }
 
 // MfmaTile<BM, BN, BK, waves along m, waves along n>
 const MfmaConfig kMfmaConfigs[] = {
-    make_cfg<MfmaTile<128, 128, 16, 2, 2>>(true),   // 0
-    make_cfg<MfmaTile<128, 128, 32, 2, 2>>(false),  // 1
-    make_cfg<MfmaTile<128, 128, 16, 2, 4>>(false),  // 2
-    make_cfg<MfmaTile<128, 128, 32, 2, 4>>(false),  // 3
-    make_cfg<MfmaTile<256, 128, 16, 2, 4>>(false),  // 4
-    make_cfg<MfmaTile<128, 256, 16, 2, 4>>(false),  // 5
-    make_cfg<MfmaTile<64, 64, 32, 2, 2>>(false),    // 6
-    make_cfg<MfmaTile<256, 128, 32, 2, 4>>(false),  // 7
-    make_cfg<MfmaTile<128, 64, 32, 2, 2>>(false),   // 8
+    make_cfg<MfmaTile<128, 128, 16, 2, 2>>(),  // 0
+    make_cfg<MfmaTile<128, 128, 32, 2, 2>>(),  // 1
+    make_cfg<MfmaTile<128, 128, 16, 2, 4>>(),  // 2
+    make_cfg<MfmaTile<128, 128, 32, 2, 4>>(),  // 3
+    make_cfg<MfmaTile<256, 128, 16, 2, 4>>(),  // 4
+    make_cfg<MfmaTile<128, 256, 16, 2, 4>>(),  // 5
+    make_cfg<MfmaTile<64, 64, 32, 2, 2>>(),    // 6
+    make_cfg<MfmaTile<256, 128, 32, 2, 4>>(),  // 7
+    make_cfg<MfmaTile<128, 64, 32, 2, 2>>(),   // 8
 };
 constexpr int kNumMfmaConfigs = sizeof(kMfmaConfigs) / sizeof(kMfmaConfigs[0]);
-constexpr int kSplitConfig = 0;  // tile configuration of the split-K partial kernel
-
 constexpr int kGroupM = 8;  // grouped-order height (the pages use groups of 8)
+constexpr int kCUs = 256;   // MI355X compute units
 
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+long long tile_count(int m, int n, int id) {
+    return ceil_div(m, kMfmaConfigs[id].bm) * ceil_div(n, kMfmaConfigs[id].bn);
+}
+
+// Largest tile that still gives every CU a workgroup (measured on MI355X:
+// 256x128x32 / 8 waves reaches 85% of the FP32 matrix peak at 8192^3 and the
+// best time on 3001x4997x1023; 128x128x32 / 8 waves 76% at 2048^3, where the
+// larger tile would leave half the CUs idle; smaller tiles for smaller C).
 int choose_mfma_config(int m, int n, int k) {
-    (void)m; (void)n; (void)k;
-    return 0;
+    (void)k;
+    if (tile_count(m, n, 7) >= kCUs) return 7;  // 256 x 128 x 32, 8 waves
+    if (tile_count(m, n, 3) >= kCUs) return 3;  // 128 x 128 x 32, 8 waves
+    if (tile_count(m, n, 8) >= kCUs) return 8;  // 128 x 64 x 32, 4 waves
+    return 6;                                   // 64 x 64 x 32, 4 waves
+}
+
+// Tile configuration of the split-K partial kernel: the largest tile that
+// still cuts C into a few tiles (slices supply the parallelism).  Measured on
+// MI355X at 512 x 512 x 262144: 256x128x32 / 8 waves with 64 slices 132.5
+// TFLOP/s, 128x128x32 / 8 waves 130.6, 64x64x32 123.8 (best slice counts).
+int choose_split_config(int m, int n, int k) {
+    (void)k;
+    if (tile_count(m, n, 7) >= 4) return 7;  // 256 x 128 x 32, 8 waves
+    if (tile_count(m, n, 8) >= 4) return 8;  // 128 x 64 x 32, 4 waves
+    return 6;                                // 64 x 64 x 32, 4 waves
 }
 
 // ---------------------------------------------------------------------------
@@ -69,18 +91,16 @@ struct SplitPlan {
 
 constexpr size_t kWsAlign = 256;
 
-long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
-
-SplitPlan plan_split(int m, int n, int k, int splits) {
+SplitPlan plan_split(int m, int n, int k, int splits, int config) {
     SplitPlan sp{0, 0, 0, 0};
     if (m <= 0 || n <= 0 || k <= 0) return sp;
-    const MfmaConfig &c = kMfmaConfigs[kSplitConfig];
+    const MfmaConfig &c = kMfmaConfigs[config];
     const long long tiles = ceil_div(m, c.bm) * ceil_div(n, c.bn);
     long long want = splits;
     if (want == 0) {
-        // Aim at about four workgroups per CU (256 CUs), with slices of at
-        // least 8 k steps.
-        const long long target_wg = 1024;
+        // Aim at about two workgroups per CU, with slices of at least 8 k
+        // steps (the combine then reads 2 * 256 partial tiles at most).
+        const long long target_wg = 2 * kCUs;
         want = ceil_div(target_wg, tiles);
         const long long max_by_k = ceil_div(k, 8LL * c.bk);
         if (want > max_by_k) want = max_by_k;
@@ -214,6 +234,50 @@ int run_valu(int config, int m, int n, int k, float alpha, const float *A, int l
     return launch(fn, grid, ValuTile::NT, s, a);
 }
 
+int run_splitk(int config, int m, int n, int k, float alpha, const float *A, int lda,
+               const float *B, int ldb, float beta, float *C, int ldc, int splits, void *ws,
+               size_t ws_bytes, void *stream) {
+    if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
+    int st = check_sizes(m, n, k, lda, ldb, ldc);
+    if (st) return st;
+    if (splits < 0 || splits > k) return MI_SGEMM_ERROR_INVALID_VALUE;
+    st = check_pointers(m, n, k, alpha, A, B, C);
+    if (st) return st;
+    if (m == 0 || n == 0) return MI_SGEMM_SUCCESS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k == 0 || alpha == 0.f) {
+        st = check_device();
+        return st ? st : launch_scale(m, n, beta, C, ldc, s);
+    }
+    const int id = config < 0 ? choose_split_config(m, n, k) : config;
+    const SplitPlan sp = plan_split(m, n, k, splits, id);
+    if (!ws || ws_bytes < sp.bytes) return MI_SGEMM_ERROR_WORKSPACE;
+    st = check_device();
+    if (st) return st;
+
+    float *wsa = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + kWsAlign - 1) &
+                                           ~(uintptr_t)(kWsAlign - 1));
+    const MfmaConfig &c = kMfmaConfigs[id];
+    GemmArgs a = base_args(m, n, k, 1.f, A, lda, B, ldb, 0.f, nullptr, ldc);
+    a.tiles_m = (int)ceil_div(m, c.bm);
+    a.tiles_n = (int)ceil_div(n, c.bn);
+    a.k_per_split = sp.k_per_split;
+    a.ws = wsa;
+    a.ws_slice = sp.slice;
+    const long long grid = (long long)a.tiles_m * a.tiles_n * sp.splits;
+    st = launch(vector_ok(A, lda, B, ldb) ? c.split_vec : c.split_scalar, grid,
+                64 * c.wgm * c.wgn, s, a);
+    if (st) return st;
+
+    const long long chunks = ceil_div((long long)m * n, 64);
+    const long long blocks = ceil_div(chunks, 4);
+    if (blocks > INT_MAX) return MI_SGEMM_ERROR_INVALID_VALUE;
+    hipLaunchKernelGGL(splitk_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const float *)wsa, sp.slice, sp.splits, m, n, alpha, beta, C,
+                       (long long)ldc);
+    return hipGetLastError() == hipSuccess ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_LAUNCH;
+}
+
 }  // namespace
 }  // namespace mi
 
@@ -242,50 +306,28 @@ int mi_sgemm_with_config(int kernel, int config, int m, int n, int k, float alph
 }
 
 size_t mi_sgemm_splitk_workspace_bytes(int m, int n, int k, int splits) {
-    if (m < 0 || n < 0 || k < 0 || splits < 0 || splits > k) return 0;
-    return plan_split(m, n, k, splits).bytes;
+    return mi_sgemm_splitk_with_config_workspace_bytes(-1, m, n, k, splits);
 }
 
 int mi_sgemm_splitk(int m, int n, int k, float alpha, const float *A, int lda, const float *B,
                     int ldb, float beta, float *C, int ldc, int splits, void *ws,
                     size_t ws_bytes, void *stream) {
-    int st = check_sizes(m, n, k, lda, ldb, ldc);
-    if (st) return st;
-    if (splits < 0 || splits > k) return MI_SGEMM_ERROR_INVALID_VALUE;
-    st = check_pointers(m, n, k, alpha, A, B, C);
-    if (st) return st;
-    if (m == 0 || n == 0) return MI_SGEMM_SUCCESS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (k == 0 || alpha == 0.f) {
-        st = check_device();
-        return st ? st : launch_scale(m, n, beta, C, ldc, s);
-    }
-    const SplitPlan sp = plan_split(m, n, k, splits);
-    if (!ws || ws_bytes < sp.bytes) return MI_SGEMM_ERROR_WORKSPACE;
-    st = check_device();
-    if (st) return st;
+    return run_splitk(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws, ws_bytes,
+                      stream);
+}
 
-    float *wsa = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + kWsAlign - 1) &
-                                           ~(uintptr_t)(kWsAlign - 1));
-    const MfmaConfig &c = kMfmaConfigs[kSplitConfig];
-    GemmArgs a = base_args(m, n, k, 1.f, A, lda, B, ldb, 0.f, nullptr, ldc);
-    a.tiles_m = (int)ceil_div(m, c.bm);
-    a.tiles_n = (int)ceil_div(n, c.bn);
-    a.k_per_split = sp.k_per_split;
-    a.ws = wsa;
-    a.ws_slice = sp.slice;
-    const long long grid = (long long)a.tiles_m * a.tiles_n * sp.splits;
-    st = launch(vector_ok(A, lda, B, ldb) ? c.split_vec : c.split_scalar, grid,
-                64 * c.wgm * c.wgn, s, a);
-    if (st) return st;
+int mi_sgemm_splitk_with_config(int config, int m, int n, int k, float alpha, const float *A,
+                                int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                                int splits, void *ws, size_t ws_bytes, void *stream) {
+    return run_splitk(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws, ws_bytes,
+                      stream);
+}
 
-    const long long chunks = ceil_div((long long)m * n, 64);
-    const long long blocks = ceil_div(chunks, 4);
-    if (blocks > INT_MAX) return MI_SGEMM_ERROR_INVALID_VALUE;
-    hipLaunchKernelGGL(splitk_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       (const float *)wsa, sp.slice, sp.splits, m, n, alpha, beta, C,
-                       (long long)ldc);
-    return hipGetLastError() == hipSuccess ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_LAUNCH;
+size_t mi_sgemm_splitk_with_config_workspace_bytes(int config, int m, int n, int k, int splits) {
+    if (m < 0 || n < 0 || k < 0 || splits < 0 || splits > k || config >= kNumMfmaConfigs)
+        return 0;
+    const int id = config < 0 ? choose_split_config(m, n, k) : config;
+    return plan_split(m, n, k, splits, id).bytes;
 }
 
 const char *mi_status_string(int status) {
@@ -304,7 +346,7 @@ const char *mi_status_string(int status) {
 int mi_sgemm_config_count(int kernel) {
     if (kernel == MI_SGEMM_KERNEL_MFMA) return kNumMfmaConfigs;
     if (kernel == MI_SGEMM_KERNEL_VALU) return 1;
-    if (kernel == MI_SGEMM_KERNEL_SPLITK) return 1;
+    if (kernel == MI_SGEMM_KERNEL_SPLITK) return kNumMfmaConfigs;
     return 0;
 }
 
@@ -329,8 +371,9 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
     } else if (kernel == MI_SGEMM_KERNEL_MFMA || kernel == MI_SGEMM_KERNEL_SPLITK) {
         int id;
         if (kernel == MI_SGEMM_KERNEL_SPLITK) {
-            if (config > 0 || splits < 0 || splits > k) return MI_SGEMM_ERROR_INVALID_VALUE;
-            id = kSplitConfig;
+            if (config >= kNumMfmaConfigs || splits < 0 || splits > k)
+                return MI_SGEMM_ERROR_INVALID_VALUE;
+            id = config < 0 ? choose_split_config(m, n, k) : config;
         } else {
             if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
             id = config < 0 ? choose_mfma_config(m, n, k) : config;
@@ -344,7 +387,7 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
         plan->fma_per_small_iteration = (plan->micro_m / 32) * (plan->micro_n / 32);
         plan->outputs_per_thread = plan->micro_m * plan->micro_n / 64;
         if (kernel == MI_SGEMM_KERNEL_SPLITK) {
-            const SplitPlan sp = plan_split(m, n, k, splits);
+            const SplitPlan sp = plan_split(m, n, k, splits, id);
             plan->splits = sp.splits;
             plan->k_per_split = sp.k_per_split;
             plan->workspace_bytes = sp.bytes;

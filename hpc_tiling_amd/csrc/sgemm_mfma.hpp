@@ -5,12 +5,12 @@
 //   * a workgroup of WGM x WGN waves owns a BM x BN tile of C and walks k in
 //     steps of BK ("big iterations");
 //   * each step stages a BM x BK tile of A and a BK x BN tile of B in one of
-//     three LDS buffers.  Interior tiles use gfx950's direct global->LDS loads
-//     (buffer_load_dwordx4 ... lds: 16 bytes per lane, no VGPRs involved), issued
-//     two steps ahead; tiles on the m/n edge, the partial last k step and
-//     unaligned operands use 16-byte (or element) loads through VGPRs with
-//     out-of-range elements stored as zeros (page aerisun.top, section
-//     "Shared Tiling 与 block 内复用");
+//     three LDS buffers.  Whole k steps of aligned operands use gfx950's
+//     direct global->LDS loads (buffer_load_dwordx4 ... lds: 16 bytes per
+//     lane, no VGPRs involved), issued two steps ahead; the partial last k
+//     step and unaligned operands use 16-byte (or element) loads through
+//     VGPRs with out-of-range elements stored as zeros (page aerisun.top,
+//     section "Shared Tiling 与 block 内复用");
 //   * each wave owns a (BM/WGM) x (BN/WGN) sub-tile held as 32 x 32 blocks
 //     of v_mfma_f32_32x32x2_f32 accumulators and reads its A and B fragments
 //     from LDS one group of 8 k ahead of the MFMAs that use them.
@@ -141,13 +141,16 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     const int kbeg = SPLIT ? slice * p.k_per_split : 0;
     const int kend = SPLIT ? min(p.k, kbeg + p.k_per_split) : p.k;
     const int nsteps = (kend - kbeg + T::BK - 1) / T::BK;
-    const bool full_m = m0 + T::BM <= p.m;
-    const bool full_n = n0 + T::BN <= p.n;
-    // Steps whose tiles are complete and aligned are loaded directly into LDS
-    // (byte offsets inside one tile step must fit the 31-bit buffer offset).
-    const bool direct_ok = VEC && full_m && full_n &&
-                           p.lda < (1LL << 31) / (4LL * T::BM) && p.ldb < (1LL << 31) / (4LL * T::BK);
+    // Whole k steps of aligned operands are loaded directly into LDS (byte
+    // offsets inside one tile step must fit the 31-bit buffer offset).  On
+    // the m / n edge, rows of A past m and chunks of B past n are clamped to
+    // the last valid row / chunk: they only feed outputs that are never
+    // stored, and every address stays inside the operands.
+    const bool direct_ok = VEC && p.lda < (1LL << 31) / (4LL * T::BM) &&
+                           p.ldb < (1LL << 31) / (4LL * T::BK);
     const int ndirect = direct_ok ? (kend - kbeg) / T::BK : 0;
+    const int a_row_max = min(T::BM, p.m - m0) - 1;           // last valid row of the A tile
+    const int b_chunk_max = (min(T::BN, p.n - n0) - 1) >> 2;  // chunk holding column n-1
 
     const float *Ablk = p.A + (long long)m0 * p.lda;
     const float *Bblk = p.B + n0;
@@ -181,14 +184,14 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
             int row, c;
             a_chunk(i, row, c);
             load_lds16(abase, as + (i * T::WAVES + wave) * 256,
-                       (int)(4 * ((long long)row * p.lda + 4 * c)));
+                       (int)(4 * ((long long)min(row, a_row_max) * p.lda + 4 * c)));
         }
 #pragma unroll
         for (int i = 0; i < T::B_PER; ++i) {
             int row, c;
             b_chunk(i, row, c);
             load_lds16(bbase, bs + (i * T::WAVES + wave) * 256,
-                       (int)(4 * ((long long)row * p.ldb + 4 * c)));
+                       (int)(4 * ((long long)row * p.ldb + 4 * min(c, b_chunk_max))));
         }
     };
 

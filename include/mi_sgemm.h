@@ -60,10 +60,11 @@ typedef enum mi_status {
  * mi_sgemm -- the matrix-core path.
  * Blocked through the memory hierarchy as described on page "GEMM优化原理",
  * sections "从 global memory 到 shared memory 再到 register" and
- * "prefetch 和双缓冲": workgroup tiles of C staged through double-buffered LDS,
- * per-wave tiles accumulated by FP32 MFMA instructions, and a grouped,
- * XCD-aware workgroup order for L2 reuse (page "gemm优化", section
- * 杂项：预取缓存1， Swizzle 增强L2缓存命中).
+ * "prefetch 和双缓冲": workgroup tiles of A and B prefetched two k steps ahead
+ * into a three-buffer LDS ring, per-wave tiles of C accumulated by FP32 MFMA
+ * instructions, and a grouped, XCD-aware workgroup order for L2 reuse (page
+ * "gemm优化", section 杂项：预取缓存1， Swizzle 增强L2缓存命中).  The tile
+ * configuration is chosen from the sizes of C (mi_sgemm_get_plan reports it).
  * Arguments: m, n, k >= 0 sizes; alpha, beta scalars; A, B read-only inputs;
  * C input (when beta != 0) and output; lda, ldb, ldc leading dimensions in
  * elements; stream a hipStream_t or NULL.  Returns a mi_status.
@@ -79,7 +80,8 @@ int mi_sgemm(int m, int n, int k, float alpha,
  * an 8 x 8 block of C updated by outer products of 8 A and 8 B values
  * (page aerisun.top, section "Register Tiling 与线程内复用"), with a
  * double-buffered LDS stage.  Same arguments, semantics and errors as
- * mi_sgemm.
+ * mi_sgemm.  Its peak is that of wave64 FP32 FMA without packed math, half
+ * the FP32 matrix rate.
  */
 int mi_sgemm_valu(int m, int n, int k, float alpha,
                   const float *A, int lda, const float *B, int ldb,
@@ -165,7 +167,8 @@ typedef struct mi_sgemm_plan {
 int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
                       mi_sgemm_plan *plan);
 
-/* Number of tile configurations of `kernel` that can be forced (ids 0..count-1). */
+/* Number of tile configurations of `kernel` that can be forced (ids 0..count-1);
+ * the split-K partial kernel takes the MI_SGEMM_KERNEL_MFMA ids. */
 int mi_sgemm_config_count(int kernel);
 
 /*
@@ -179,6 +182,20 @@ int mi_sgemm_config_count(int kernel);
 int mi_sgemm_with_config(int kernel, int config, int m, int n, int k, float alpha,
                          const float *A, int lda, const float *B, int ldb,
                          float beta, float *C, int ldc, void *stream);
+
+/*
+ * mi_sgemm_splitk_with_config -- mi_sgemm_splitk with a forced tile
+ * configuration of the partial kernel (ids as for MI_SGEMM_KERNEL_MFMA;
+ * config < 0 means the automatic choice).  The workspace it needs is given
+ * by mi_sgemm_splitk_with_config_workspace_bytes (0 for invalid arguments or
+ * an unknown config).  Same semantics and errors as mi_sgemm_splitk.
+ */
+int mi_sgemm_splitk_with_config(int config, int m, int n, int k, float alpha,
+                                const float *A, int lda, const float *B, int ldb,
+                                float beta, float *C, int ldc,
+                                int splits, void *ws, size_t ws_bytes, void *stream);
+size_t mi_sgemm_splitk_with_config_workspace_bytes(int config, int m, int n, int k,
+                                                   int splits);
 
 #ifdef __cplusplus
 }

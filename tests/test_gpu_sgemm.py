@@ -49,6 +49,10 @@ def run_kernel(kind, A, B, C, alpha, beta):
         hta.sgemm_valu(A, B, C, alpha, beta)
     elif kind == "splitk":
         hta.sgemm_splitk(A, B, C, alpha, beta, splits=0)
+    elif kind.startswith("splitk_cfg"):
+        # forced partial-kernel tiles with an odd slice count (at most k)
+        splits = min(5, A.shape[1])
+        hta.sgemm_splitk(A, B, C, alpha, beta, splits=splits, config=int(kind[len("splitk_cfg"):]))
     elif kind.startswith("splitk"):
         # a split count above k is an argument error; ask for at most k slices
         splits = min(int(kind[len("splitk"):]), A.shape[1])
@@ -120,7 +124,8 @@ def sampled_check(orc, kind, w, integer, nrows, seed=0):
 # Small ragged shapes on every path and every tile configuration
 # ---------------------------------------------------------------------------
 KINDS = (["mfma", "valu", "splitk", "splitk3", "splitk1"]
-         + [f"mfma_cfg{i}" for i in range(N_MFMA_CFG)])
+         + [f"mfma_cfg{i}" for i in range(N_MFMA_CFG)]
+         + [f"splitk_cfg{i}" for i in range(N_MFMA_CFG)])
 SHAPES = [(1, 1, 1), (7, 9, 5), (33, 65, 17), (130, 257, 300), (255, 129, 64), (64, 128, 2049)]
 
 
