@@ -62,51 +62,6 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-def sclk_mhz():
-    """Current shader clock from sysfs (the level marked '*'), when readable."""
-    import glob
-    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            for line in open(f):
-                if "*" in line:
-                    return float(line.split(":")[1].strip().rstrip("*").strip().rstrip("Mhz").strip())
-        except (OSError, ValueError, IndexError):
-            continue
-    return None
-
-
-class ClockSampler:
-    """Polls the shader clock from a host thread while the GPU works."""
-
-    def __init__(self, period_s=0.002):
-        import threading
-        self.period = period_s
-        self.samples = []
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-
-    def _run(self):
-        while not self._stop.is_set():
-            v = sclk_mhz()
-            if v is not None:
-                self.samples.append(v)
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        self._thread.join()
-
-    def summary(self):
-        if not self.samples:
-            return None
-        v = sorted(self.samples)
-        return {"samples": len(v), "min": v[0], "median": v[len(v) // 2], "max": v[-1]}
-
-
 def make_step(kind, w, Av, Bv, Cv, ws):
     import hpc_tiling_amd as hta
     alpha, beta = w.alpha, w.beta
@@ -195,8 +150,9 @@ def _cpu_model():
     return None
 
 
-def secondary(kinds_workloads, reps=10):
-    """TFLOP/s of other (kernel, workload) pairs, a few calls each."""
+def secondary(kinds_workloads, seconds=0.25):
+    """TFLOP/s of other (kernel, workload) pairs, each timed over about
+    `seconds` of back-to-back calls after a short warmup."""
     import torch
     import synth
     from hpc_tiling_amd import perfmodel as pm
@@ -204,8 +160,9 @@ def secondary(kinds_workloads, reps=10):
     for kind, name in kinds_workloads:
         w = synth.workload(name)
         host, dev, step = setup(w, kind)
-        n = max(2, min(reps, int(2e13 // max(w.flops, 1))))
-        dt = time_steps(step, n, warmup=2)
+        probe = time_steps(step, 2, warmup=2) / 2
+        n = max(3, min(2000, int(seconds / max(probe, 1e-6))))
+        dt = time_steps(step, n, warmup=5)
         tf = pm.tflops(w.m, w.n, w.k, dt, reps=n)
         out.append({"workload": name, "kernel": kind, "ms_per_call": 1e3 * dt / n,
                     "tflops": tf, "frac_of_fp32_peak": tf * 1e12 / pm.PEAK_FP32_MFMA})
@@ -258,8 +215,7 @@ def main(argv=None):
     print(f"[bench] {kind} {w.name}: generating operands", file=sys.stderr, flush=True)
     host, dev, step = setup(w, kind)
     print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
-    with ClockSampler() as clocks:
-        dt = time_steps(step, args.steps, args.warmup)
+    dt = time_steps(step, args.steps, args.warmup)
     ms = 1e3 * dt / args.steps
     value = pm.tflops(w.m, w.n, w.k, dt, reps=args.steps)
 
@@ -296,7 +252,6 @@ def main(argv=None):
                    "ldc": w.ldc, "alpha": w.alpha, "beta": w.beta, "kernel": kind,
                    "layout": "row-major"},
         "frac_of_fp32_peak": value * 1e12 / pm.PEAK_FP32_MFMA,
-        "sclk_mhz": clocks.summary(),
         "roofline": roof,
     }
     del dev, step
