@@ -45,6 +45,7 @@ const MfmaConfig kMfmaConfigs[] = {
     make_cfg<MfmaTile<64, 64, 32, 2, 2>>(),    // 6
     make_cfg<MfmaTile<256, 128, 32, 2, 4>>(),  // 7
     make_cfg<MfmaTile<128, 64, 32, 2, 2>>(),   // 8
+    make_cfg<MfmaTile<128, 128, 32, 4, 4>>(),  // 9
 };
 constexpr int kNumMfmaConfigs = sizeof(kMfmaConfigs) / sizeof(kMfmaConfigs[0]);
 constexpr int kGroupM = 8;  // grouped-order height (the pages use groups of 8)

@@ -335,7 +335,16 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
                 default: one_step(step, direct_tag, std::integral_constant<int, 2>{}); break;
             }
         };
+        using S2 = std::integral_constant<int, 2>;
         int step = 0;
+        // Steady state: three steps per iteration, so each ring position is a
+        // compile-time constant and the accumulators keep their registers
+        // (a runtime switch per step makes the compiler copy them around).
+        for (; step + 4 < ndirect; step += 3) {
+            one_step(step, std::true_type{}, S0{});
+            one_step(step + 1, std::true_type{}, S1{});
+            one_step(step + 2, std::true_type{}, S2{});
+        }
         for (; step + 2 < ndirect; ++step) dispatch(step, std::true_type{});
         for (; step < nsteps; ++step) dispatch(step, std::false_type{});
     }
