@@ -57,25 +57,51 @@ long long tile_count(int m, int n, int id) {
     return ceil_div(m, kMfmaConfigs[id].bm) * ceil_div(n, kMfmaConfigs[id].bn);
 }
 
-// Largest tile that still gives every CU a workgroup (measured on MI355X:
-// 256x128x32 / 8 waves reaches 85% of the FP32 matrix peak at 8192^3 and the
-// best time on 3001x4997x1023; 128x128x32 / 8 waves 76% at 2048^3, where the
-// larger tile would leave half the CUs idle; smaller tiles for smaller C).
-int choose_mfma_config(int m, int n, int k) {
-    (void)k;
-    if (tile_count(m, n, 7) >= kCUs) return 7;  // 256 x 128 x 32, 8 waves
-    if (tile_count(m, n, 3) >= kCUs) return 3;  // 128 x 128 x 32, 8 waves
-    if (tile_count(m, n, 8) >= kCUs) return 8;  // 128 x 64 x 32, 4 waves
-    return 6;                                   // 64 x 64 x 32, 4 waves
+// Tile choice: a small cost model.  The workgroups of a launch are spread
+// evenly over the CUs, so the busiest CU runs ceil(tiles / CUs) tiles; its
+// time is that count times the tile area over the configuration's efficiency
+// when every CU is busy.  The efficiencies are measured on MI355X at 4096^3,
+// where every configuration divides the grid evenly (fraction of the FP32
+// matrix peak); ties go to the earlier entry.
+struct Candidate {
+    int id;
+    double efficiency;
+};
+constexpr Candidate kCandidates[] = {
+    {9, 0.946},  // 128 x 128 x 32, 16 waves
+    {0, 0.941},  // 128 x 128 x 16, 4 waves
+    {7, 0.937},  // 256 x 128 x 32, 8 waves
+    {8, 0.922},  // 128 x 64 x 32, 4 waves
+    {6, 0.906},  // 64 x 64 x 32, 4 waves
+};
+
+double tile_cost(int m, int n, int id, double efficiency) {
+    const MfmaConfig &c = kMfmaConfigs[id];
+    const long long per_cu = ceil_div(tile_count(m, n, id), kCUs);
+    return (double)per_cu * c.bm * c.bn / efficiency;
 }
 
-// Tile configuration of the split-K partial kernel: the largest tile that
-// still cuts C into a few tiles (slices supply the parallelism).  Measured on
-// MI355X at 512 x 512 x 262144: 256x128x32 / 8 waves with 64 slices 132.5
-// TFLOP/s, 128x128x32 / 8 waves 130.6, 64x64x32 123.8 (best slice counts).
+int choose_mfma_config(int m, int n, int k) {
+    (void)k;
+    int best = kCandidates[0].id;
+    double best_cost = tile_cost(m, n, best, kCandidates[0].efficiency);
+    for (const Candidate &cand : kCandidates) {
+        const double cost = tile_cost(m, n, cand.id, cand.efficiency);
+        if (cost < best_cost * 0.999) {
+            best = cand.id;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+// Tile configuration of the split-K partial kernel: the 128 x 128 x 32,
+// 16-wave tile when C holds at least a few of them (slices then supply the
+// parallelism), smaller tiles for small C.  Measured on MI355X at 512 x 512 x
+// 262144 with one round of workgroups: 143.5 TFLOP/s (16 slices).
 int choose_split_config(int m, int n, int k) {
     (void)k;
-    if (tile_count(m, n, 7) >= 4) return 7;  // 256 x 128 x 32, 8 waves
+    if (tile_count(m, n, 9) >= 4) return 9;  // 128 x 128 x 32, 16 waves
     if (tile_count(m, n, 8) >= 4) return 8;  // 128 x 64 x 32, 4 waves
     return 6;                                // 64 x 64 x 32, 4 waves
 }
@@ -99,9 +125,9 @@ SplitPlan plan_split(int m, int n, int k, int splits, int config) {
     const long long tiles = ceil_div(m, c.bm) * ceil_div(n, c.bn);
     long long want = splits;
     if (want == 0) {
-        // Aim at about two workgroups per CU, with slices of at least 8 k
-        // steps (the combine then reads 2 * 256 partial tiles at most).
-        const long long target_wg = 2 * kCUs;
+        // One round of workgroups (one per CU), with slices of at least 8 k
+        // steps.
+        const long long target_wg = kCUs;
         want = ceil_div(target_wg, tiles);
         const long long max_by_k = ceil_div(k, 8LL * c.bk);
         if (want > max_by_k) want = max_by_k;
