@@ -71,6 +71,8 @@ def make_step(kind, w, Av, Bv, Cv, ws):
         return lambda: hta.sgemm_valu(Av, Bv, Cv, alpha, beta)
     if kind == "splitk":
         return lambda: hta.sgemm_splitk(Av, Bv, Cv, alpha, beta, splits=0, workspace=ws)
+    if kind == "splitk_atomic":
+        return lambda: hta.sgemm_splitk_atomic(Av, Bv, Cv, alpha, beta, splits=0)
     if kind.startswith("mfma_cfg"):
         cfg = int(kind[len("mfma_cfg"):])
         return lambda: hta.sgemm(Av, Bv, Cv, alpha, beta, config=cfg)
@@ -177,7 +179,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--kernel", default="mfma", help="mfma | valu | splitk | mfma_cfgN")
+    ap.add_argument("--kernel", default="mfma",
+                    help="mfma | valu | splitk | splitk_atomic | mfma_cfgN")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -260,7 +263,8 @@ def main(argv=None):
     if not args.no_secondary:
         print("[bench] secondary workloads", file=sys.stderr, flush=True)
         pairs = [("mfma", "sgemm_8192x8192x8192_ab"), ("mfma", "sgemm_tails_3001x4997x1023"),
-                 ("splitk", "sgemm_splitk_512x512x262144"), ("valu", "sgemm_2048x2048x2048"),
+                 ("splitk", "sgemm_splitk_512x512x262144"),
+                 ("splitk_atomic", "sgemm_splitk_512x512x262144"), ("valu", "sgemm_2048x2048x2048"),
                  ("mfma", "sgemm_256x256x256")]
         line["secondary"] = secondary(pairs)
 

@@ -20,8 +20,9 @@ __all__ = [
     "mi_sgemm", "mi_sgemm_valu", "mi_sgemm_splitk", "mi_sgemm_splitk_workspace_bytes",
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
-    "sgemm", "sgemm_valu", "sgemm_splitk", "splitk_workspace",
-    "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "EXPORTED_SYMBOLS",
+    "mi_sgemm_splitk_atomic",
+    "sgemm", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace",
+    "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "KERNEL_SPLITK_ATOMIC", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libmi_sgemm.so"
@@ -37,11 +38,13 @@ ERROR_DEVICE = 6
 KERNEL_MFMA = 0
 KERNEL_VALU = 1
 KERNEL_SPLITK = 2
+KERNEL_SPLITK_ATOMIC = 3
 
 EXPORTED_SYMBOLS = (
     "mi_sgemm", "mi_sgemm_valu", "mi_sgemm_splitk_workspace_bytes", "mi_sgemm_splitk",
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
+    "mi_sgemm_splitk_atomic",
 )
 
 if not LIB_PATH.exists():
@@ -96,6 +99,8 @@ lib.mi_sgemm_splitk_with_config.argtypes = [_i] + _GEMM_ARGS + [_i, _vp, _sz, _v
 lib.mi_sgemm_splitk_with_config.restype = _i
 lib.mi_sgemm_splitk_with_config_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.mi_sgemm_splitk_with_config_workspace_bytes.restype = _sz
+lib.mi_sgemm_splitk_atomic.argtypes = _GEMM_ARGS + [_i, _vp]
+lib.mi_sgemm_splitk_atomic.restype = _i
 lib.mi_status_string.argtypes = [_i]
 lib.mi_status_string.restype = ctypes.c_char_p
 lib.mi_sgemm_get_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(Plan)]
@@ -145,6 +150,12 @@ def mi_sgemm_splitk_with_config(config, m, n, k, alpha, A, lda, B, ldb, beta, C,
 
 def mi_sgemm_splitk_with_config_workspace_bytes(config, m, n, k, splits=0) -> int:
     return lib.mi_sgemm_splitk_with_config_workspace_bytes(config, m, n, k, splits)
+
+
+def mi_sgemm_splitk_atomic(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits=0,
+                           stream=None) -> int:
+    return lib.mi_sgemm_splitk_atomic(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                                      stream)
 
 
 def mi_status_string(status: int) -> str:
@@ -261,4 +272,15 @@ def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, st
                                              _stream(stream))
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_splitk")
+    return C
+
+
+def sgemm_splitk_atomic(A, B, C=None, alpha=1.0, beta=0.0, splits=0, stream=None):
+    """Split-K with atomic accumulation into C (no workspace; not bitwise
+    reproducible run to run)."""
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
+    st = lib.mi_sgemm_splitk_atomic(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
+                                    _stream(stream))
+    if st != SUCCESS:
+        raise MiSgemmError(st, "mi_sgemm_splitk_atomic")
     return C

@@ -10,6 +10,9 @@ namespace mi {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Epilogue modes of the matrix-core kernel (see sgemm_mfma.hpp).
+constexpr int kFull = 0, kPartial = 1, kAtomic = 2;
+
 // MI355X places workgroups on its 8 XCDs (each with a private L2) round-robin
 // by workgroup id.
 constexpr int kXcds = 8;

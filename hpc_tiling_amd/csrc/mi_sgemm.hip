@@ -23,15 +23,17 @@ using KernelFn = void (*)(GemmArgs);
 // ---------------------------------------------------------------------------
 struct MfmaConfig {
     int bm, bn, bk, wgm, wgn;
-    KernelFn vec, scalar;              // full-k kernels
-    KernelFn split_vec, split_scalar;  // split-K partial kernels
+    KernelFn vec, scalar;                // full-k kernels
+    KernelFn split_vec, split_scalar;    // split-K partial kernels
+    KernelFn atomic_vec, atomic_scalar;  // split-K kernels adding into C atomically
 };
 
 template <class T>
 constexpr MfmaConfig make_cfg() {
     return MfmaConfig{T::BM, T::BN, T::BK, T::WGM, T::WGN,
-                      &sgemm_mfma_kernel<T, true, false>, &sgemm_mfma_kernel<T, false, false>,
-                      &sgemm_mfma_kernel<T, true, true>, &sgemm_mfma_kernel<T, false, true>};
+                      &sgemm_mfma_kernel<T, true, kFull>, &sgemm_mfma_kernel<T, false, kFull>,
+                      &sgemm_mfma_kernel<T, true, kPartial>, &sgemm_mfma_kernel<T, false, kPartial>,
+                      &sgemm_mfma_kernel<T, true, kAtomic>, &sgemm_mfma_kernel<T, false, kAtomic>};
 }
 
 // MfmaTile<BM, BN, BK, waves along m, waves along n>
@@ -181,24 +183,27 @@ bool vector_ok(const float *A, int lda, const float *B, int ldb) {
     return aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0;
 }
 
-int launch(KernelFn fn, long long grid, int threads, hipStream_t stream, GemmArgs args) {
+// Every launch reports the status hipLaunchKernel itself returns (not a
+// sticky error another library may have left behind).
+int launch_raw(const void *fn, long long grid, int threads, void **args, hipStream_t stream) {
     if (grid <= 0) return MI_SGEMM_SUCCESS;
     if (grid > INT_MAX) return MI_SGEMM_ERROR_INVALID_VALUE;
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), args, 0, stream) == hipSuccess
+               ? MI_SGEMM_SUCCESS
+               : MI_SGEMM_ERROR_LAUNCH;
+}
+
+int launch(KernelFn fn, long long grid, int threads, hipStream_t stream, GemmArgs args) {
     void *kargs[] = {&args};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid),
-                                   dim3(threads), kargs, 0, stream);
-    if (e != hipSuccess) return MI_SGEMM_ERROR_LAUNCH;
-    e = hipGetLastError();
-    return e == hipSuccess ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_LAUNCH;
+    return launch_raw(reinterpret_cast<const void *>(fn), grid, threads, kargs, stream);
 }
 
 int launch_scale(int m, int n, float beta, float *C, int ldc, hipStream_t stream) {
-    const long long total = (long long)m * n;
-    long long blocks = ceil_div(total, 256);
+    long long blocks = ceil_div((long long)m * n, 256);
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(scale_c_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, m, n,
-                       beta, C, (long long)ldc);
-    return hipGetLastError() == hipSuccess ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_LAUNCH;
+    long long ldc64 = ldc;
+    void *args[] = {&m, &n, &beta, &C, &ldc64};
+    return launch_raw(reinterpret_cast<const void *>(&scale_c_kernel), blocks, 256, args, stream);
 }
 
 GemmArgs base_args(int m, int n, int k, float alpha, const float *A, int lda, const float *B,
@@ -296,13 +301,44 @@ int run_splitk(int config, int m, int n, int k, float alpha, const float *A, int
                 64 * c.wgm * c.wgn, s, a);
     if (st) return st;
 
-    const long long chunks = ceil_div((long long)m * n, 64);
-    const long long blocks = ceil_div(chunks, 4);
-    if (blocks > INT_MAX) return MI_SGEMM_ERROR_INVALID_VALUE;
-    hipLaunchKernelGGL(splitk_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       (const float *)wsa, sp.slice, sp.splits, m, n, alpha, beta, C,
-                       (long long)ldc);
-    return hipGetLastError() == hipSuccess ? MI_SGEMM_SUCCESS : MI_SGEMM_ERROR_LAUNCH;
+    const long long blocks = ceil_div(ceil_div((long long)m * n, 64), 4);
+    const float *wsc = wsa;
+    long long slice = sp.slice, ldc64 = ldc;
+    int nsplit = sp.splits;
+    void *args[] = {&wsc, &slice, &nsplit, &m, &n, &alpha, &beta, &C, &ldc64};
+    return launch_raw(reinterpret_cast<const void *>(&splitk_combine_kernel), blocks, 256, args, s);
+}
+
+// Split-K without a workspace: C <- beta*C, then every (tile, slice)
+// workgroup adds alpha * (its slice sum) into C with float atomics.
+int run_splitk_atomic(int config, int m, int n, int k, float alpha, const float *A, int lda,
+                      const float *B, int ldb, float beta, float *C, int ldc, int splits,
+                      void *stream) {
+    if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
+    int st = check_sizes(m, n, k, lda, ldb, ldc);
+    if (st) return st;
+    if (splits < 0 || splits > k) return MI_SGEMM_ERROR_INVALID_VALUE;
+    st = check_pointers(m, n, k, alpha, A, B, C);
+    if (st) return st;
+    if (m == 0 || n == 0) return MI_SGEMM_SUCCESS;
+    st = check_device();
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k == 0 || alpha == 0.f) return launch_scale(m, n, beta, C, ldc, s);
+    const int id = config < 0 ? choose_split_config(m, n, k) : config;
+    const SplitPlan sp = plan_split(m, n, k, splits, id);
+    if (beta != 1.f) {
+        st = launch_scale(m, n, beta, C, ldc, s);
+        if (st) return st;
+    }
+    const MfmaConfig &c = kMfmaConfigs[id];
+    GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
+    a.tiles_m = (int)ceil_div(m, c.bm);
+    a.tiles_n = (int)ceil_div(n, c.bn);
+    a.k_per_split = sp.k_per_split;
+    const long long grid = (long long)a.tiles_m * a.tiles_n * sp.splits;
+    return launch(vector_ok(A, lda, B, ldb) ? c.atomic_vec : c.atomic_scalar, grid,
+                  64 * c.wgm * c.wgn, s, a);
 }
 
 }  // namespace
@@ -350,6 +386,12 @@ int mi_sgemm_splitk_with_config(int config, int m, int n, int k, float alpha, co
                       stream);
 }
 
+int mi_sgemm_splitk_atomic(int m, int n, int k, float alpha, const float *A, int lda,
+                           const float *B, int ldb, float beta, float *C, int ldc, int splits,
+                           void *stream) {
+    return run_splitk_atomic(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, stream);
+}
+
 size_t mi_sgemm_splitk_with_config_workspace_bytes(int config, int m, int n, int k, int splits) {
     if (m < 0 || n < 0 || k < 0 || splits < 0 || splits > k || config >= kNumMfmaConfigs)
         return 0;
@@ -373,7 +415,8 @@ const char *mi_status_string(int status) {
 int mi_sgemm_config_count(int kernel) {
     if (kernel == MI_SGEMM_KERNEL_MFMA) return kNumMfmaConfigs;
     if (kernel == MI_SGEMM_KERNEL_VALU) return 1;
-    if (kernel == MI_SGEMM_KERNEL_SPLITK) return kNumMfmaConfigs;
+    if (kernel == MI_SGEMM_KERNEL_SPLITK || kernel == MI_SGEMM_KERNEL_SPLITK_ATOMIC)
+        return kNumMfmaConfigs;
     return 0;
 }
 
@@ -395,9 +438,11 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
         plan->small_iterations = ValuTile::BK;
         plan->fma_per_small_iteration = ValuTile::RM * ValuTile::RN;
         plan->outputs_per_thread = ValuTile::RM * ValuTile::RN;
-    } else if (kernel == MI_SGEMM_KERNEL_MFMA || kernel == MI_SGEMM_KERNEL_SPLITK) {
+    } else if (kernel == MI_SGEMM_KERNEL_MFMA || kernel == MI_SGEMM_KERNEL_SPLITK ||
+               kernel == MI_SGEMM_KERNEL_SPLITK_ATOMIC) {
         int id;
-        if (kernel == MI_SGEMM_KERNEL_SPLITK) {
+        const bool split = kernel != MI_SGEMM_KERNEL_MFMA;
+        if (split) {
             if (config >= kNumMfmaConfigs || splits < 0 || splits > k)
                 return MI_SGEMM_ERROR_INVALID_VALUE;
             id = config < 0 ? choose_split_config(m, n, k) : config;
@@ -413,11 +458,11 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
         plan->small_iterations = c.bk / 2;
         plan->fma_per_small_iteration = (plan->micro_m / 32) * (plan->micro_n / 32);
         plan->outputs_per_thread = plan->micro_m * plan->micro_n / 64;
-        if (kernel == MI_SGEMM_KERNEL_SPLITK) {
+        if (split) {
             const SplitPlan sp = plan_split(m, n, k, splits, id);
             plan->splits = sp.splits;
             plan->k_per_split = sp.k_per_split;
-            plan->workspace_bytes = sp.bytes;
+            plan->workspace_bytes = kernel == MI_SGEMM_KERNEL_SPLITK ? sp.bytes : 0;
         }
     } else {
         return MI_SGEMM_ERROR_INVALID_VALUE;

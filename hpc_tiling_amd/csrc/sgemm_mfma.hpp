@@ -83,9 +83,12 @@ __device__ __forceinline__ void load_lds16(const float *base, float *lds, int vo
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds), 16, voffset, 0, 0, 0);
 }
 
-// SPLIT: workgroup (tile, slice) sums k in [slice*k_per_split, ...) into the
-// raw partial ws[slice] (no alpha/beta); otherwise the full k range is summed
-// and C = alpha*acc + beta*C is written.  VEC: A and B allow 16-byte loads.
+// Epilogue modes.  kFull: the whole k range, C = alpha*acc + beta*C.
+// kPartial: workgroup (tile, slice) sums k in [slice*k_per_split, ...) into
+// the raw partial ws[slice] (no alpha/beta).  kAtomic: the same slice sum,
+// added as alpha*acc to C with hardware float atomics (C already holds
+// beta*C; the order of the additions, hence the last bits, varies from run
+// to run).  VEC: A and B allow 16-byte loads.
 //
 // Pipeline (one barrier per step, buffers used round-robin):
 //   top of step t    issue the tile of step t+2 into buffer (t+2) % 3 (direct
@@ -98,8 +101,9 @@ __device__ __forceinline__ void load_lds16(const float *base, float *lds, int vo
 // same barrier (which waits for the direct loads), so the first fragments of
 // step t+1 can be read before the barrier of step t and the MFMA stream does
 // not wait for LDS at a step boundary.
-template <class T, bool VEC, bool SPLIT>
+template <class T, bool VEC, int MODE>
 __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
+    constexpr bool SPLIT = MODE != kFull;
     // One LDS object per ring stage, always indexed at compile time: the
     // compiler can then tell the buffer a direct load writes from the buffers
     // being read, and does not hold the MFMAs back until the load lands.
@@ -361,8 +365,10 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * T::WTM + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
                 if (row < p.m && col < p.n) {
-                    if (SPLIT) {
+                    if constexpr (MODE == kPartial) {
                         p.ws[(long long)slice * p.ws_slice + (long long)row * p.n + col] = acc[a][b][r];
+                    } else if constexpr (MODE == kAtomic) {
+                        unsafeAtomicAdd(p.C + (long long)row * p.ldc + col, p.alpha * acc[a][b][r]);
                     } else {
                         float *dst = p.C + (long long)row * p.ldc + col;
                         float v = p.alpha * acc[a][b][r];

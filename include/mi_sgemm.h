@@ -22,7 +22,8 @@
  * `stream` is a hipStream_t (NULL = the null stream) of the current device.
  * Compute calls are asynchronous: they return once the kernels are enqueued.
  * C must not overlap A, B or the workspace.  Results are deterministic: the
- * same call on the same inputs gives the same bits.
+ * same call on the same inputs gives the same bits (mi_sgemm_splitk_atomic
+ * excepted).
  *
  * Special cases.
  *  - m == 0 or n == 0: nothing is done (no pointer is touched).
@@ -117,6 +118,22 @@ int mi_sgemm_splitk(int m, int n, int k, float alpha,
                     float beta, float *C, int ldc,
                     int splits, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * mi_sgemm_splitk_atomic -- split-K without a workspace, kept as a measured
+ * comparison for mi_sgemm_splitk: C is first scaled by beta (skipped when
+ * beta == 1; beta == 0 writes zeros without reading C), then every
+ * (tile, slice) workgroup adds alpha times its slice sum into C with hardware
+ * float atomics -- the global-atomic combine of page aerisun.top, section
+ * "全局原子操作互锁", applied once per output element and slice.  The order of
+ * the additions varies between runs, so results are NOT bitwise
+ * reproducible (they stay within the same error bound, and integer-valued
+ * sums are exact).  Other arguments and errors as mi_sgemm_splitk, without
+ * the workspace.
+ */
+int mi_sgemm_splitk_atomic(int m, int n, int k, float alpha,
+                           const float *A, int lda, const float *B, int ldb,
+                           float beta, float *C, int ldc, int splits, void *stream);
+
 /* Text for a mi_status value (a static string; never NULL). */
 const char *mi_status_string(int status);
 
@@ -127,7 +144,8 @@ const char *mi_status_string(int status);
 typedef enum mi_kernel {
     MI_SGEMM_KERNEL_MFMA = 0,
     MI_SGEMM_KERNEL_VALU = 1,
-    MI_SGEMM_KERNEL_SPLITK = 2
+    MI_SGEMM_KERNEL_SPLITK = 2,
+    MI_SGEMM_KERNEL_SPLITK_ATOMIC = 3
 } mi_kernel;
 
 /*

@@ -133,6 +133,19 @@ def test_splitk_argument_errors():
     assert f(0, 64, 1024, 1.0, None, 1024, None, 64, 0.0, None, 64, 0, None, 0) == E.SUCCESS
 
 
+def test_splitk_atomic_argument_errors():
+    E, f = hta, hta.mi_sgemm_splitk_atomic
+    assert f(-1, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4, 0) == E.ERROR_INVALID_VALUE
+    assert f(4, 4, 8, 1.0, P, 8, P, 4, 0.0, P, 4, 9) == E.ERROR_INVALID_VALUE   # splits > k
+    assert f(4, 4, 8, 1.0, P, 8, P, 4, 0.0, P, 4, -1) == E.ERROR_INVALID_VALUE
+    assert f(4, 4, 8, 1.0, P, 7, P, 4, 0.0, P, 4, 0) == E.ERROR_INVALID_LD
+    assert f(4, 4, 8, 1.0, P, 8, P, 4, 0.0, None, 4, 0) == E.ERROR_NULL_POINTER
+    assert f(0, 4, 8, 1.0, None, 8, None, 4, 0.0, None, 4, 0) == E.SUCCESS
+    p = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK_ATOMIC, -1, 512, 512, 262144, 0)
+    q = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, 512, 512, 262144, 0)
+    assert p["workspace_bytes"] == 0 and p["splits"] == q["splits"] > 1
+
+
 def test_with_config_rejects_unknown_ids():
     n = hta.mi_sgemm_config_count(hta.KERNEL_MFMA)
     assert n >= 1

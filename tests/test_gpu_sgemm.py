@@ -49,6 +49,9 @@ def run_kernel(kind, A, B, C, alpha, beta):
         hta.sgemm_valu(A, B, C, alpha, beta)
     elif kind == "splitk":
         hta.sgemm_splitk(A, B, C, alpha, beta, splits=0)
+    elif kind.startswith("splitk_atomic"):
+        splits = min(int(kind[len("splitk_atomic"):] or 0), A.shape[1])
+        hta.sgemm_splitk_atomic(A, B, C, alpha, beta, splits=splits)
     elif kind.startswith("splitk_cfg"):
         # forced partial-kernel tiles with an odd slice count (at most k)
         splits = min(5, A.shape[1])
@@ -123,7 +126,7 @@ def sampled_check(orc, kind, w, integer, nrows, seed=0):
 # ---------------------------------------------------------------------------
 # Small ragged shapes on every path and every tile configuration
 # ---------------------------------------------------------------------------
-KINDS = (["mfma", "valu", "splitk", "splitk3", "splitk1"]
+KINDS = (["mfma", "valu", "splitk", "splitk3", "splitk1", "splitk_atomic", "splitk_atomic3"]
          + [f"mfma_cfg{i}" for i in range(N_MFMA_CFG)]
          + [f"splitk_cfg{i}" for i in range(N_MFMA_CFG)])
 SHAPES = [(1, 1, 1), (7, 9, 5), (33, 65, 17), (130, 257, 300), (255, 129, 64), (64, 128, 2049)]
@@ -168,7 +171,7 @@ def test_workload_tails(orc, kind, integer):
     sampled_check(orc, kind, synth.workload(3), integer, nrows=48)
 
 
-@pytest.mark.parametrize("kind", ["splitk", "mfma"])
+@pytest.mark.parametrize("kind", ["splitk", "mfma", "splitk_atomic"])
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 def test_workload_splitk(orc, kind, integer):
     sampled_check(orc, kind, synth.workload(4), integer, nrows=6)
@@ -177,7 +180,7 @@ def test_workload_splitk(orc, kind, integer):
 # ---------------------------------------------------------------------------
 # Special cases of the interface
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
+@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk", "splitk_atomic"])
 def test_beta_zero_ignores_nan_c(kind):
     say("beta0 nan C", kind)
     m, n, k = 70, 90, 33
@@ -188,7 +191,7 @@ def test_beta_zero_ignores_nan_c(kind):
     assert torch.equal(C, torch.full((m, n), 2.0 * k, device="cuda"))
 
 
-@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
+@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk", "splitk_atomic"])
 def test_alpha_zero_and_k_zero(kind):
     say("alpha0/k0", kind)
     m, n = 45, 77
@@ -208,7 +211,7 @@ def test_alpha_zero_and_k_zero(kind):
     assert torch.equal(C.cpu(), torch.zeros((m, n)))
 
 
-@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
+@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk", "splitk_atomic"])
 def test_misaligned_operands(orc, kind):
     """Pointers one float off 16-byte alignment take the element-load path."""
     say("misaligned", kind)
@@ -286,3 +289,12 @@ def test_non_default_stream():
     s.synchronize()
     assert torch.equal(C, torch.full((m, n), float(k), device="cuda"))
     assert torch.equal(D, torch.full((m, n), float(k), device="cuda"))
+
+
+def test_splitk_atomic_beta_one_and_tolerance(orc):
+    """beta == 1 skips the scaling pass (C accumulates in place); results of
+    the atomic variant stay within the bar of the oracle."""
+    say("splitk atomic beta=1")
+    w = synth.workload(3).scaled(dist_c="uniform", alpha=-0.5, beta=1.0)
+    sampled_check(orc, "splitk_atomic", w, integer=False, nrows=16)
+    sampled_check(orc, "splitk_atomic", w, integer=True, nrows=16)
