@@ -173,6 +173,29 @@ def secondary(kinds_workloads, seconds=0.25):
     return out
 
 
+def reduce_secondary(name="reduce_sum_268435456", seconds=0.25):
+    """The array sum on its largest workload: GB/s of algorithmic bytes (4n)
+    and the fraction of the 8 TB/s HBM roofline."""
+    import torch
+    import hpc_tiling_amd as hta
+    import synth
+    from hpc_tiling_amd import perfmodel as pm
+    x = torch.from_numpy(synth.vector(name)).to("cuda")
+    out = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(hta.mi_reduce_sum_workspace_bytes(x.numel()), 4), dtype=torch.uint8,
+                     device="cuda")
+    step = lambda: hta.reduce_sum(x, out=out, workspace=ws)
+    probe = time_steps(step, 2, warmup=2) / 2
+    n = max(3, min(5000, int(seconds / max(probe, 1e-6))))
+    dt = time_steps(step, n, warmup=5) / n
+    gbs = 4.0 * x.numel() / dt / 1e9
+    res = {"workload": name, "kernel": "reduce_sum", "us_per_call": 1e6 * dt, "gb_per_s": gbs,
+           "frac_of_hbm_peak": gbs * 1e9 / pm.PEAK_HBM_BYTES}
+    del x, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,6 +290,7 @@ def main(argv=None):
                  ("splitk_atomic", "sgemm_splitk_512x512x262144"), ("valu", "sgemm_2048x2048x2048"),
                  ("mfma", "sgemm_256x256x256")]
         line["secondary"] = secondary(pairs)
+        line["secondary"].append(reduce_secondary())
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

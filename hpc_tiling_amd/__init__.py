@@ -20,8 +20,9 @@ __all__ = [
     "mi_sgemm", "mi_sgemm_valu", "mi_sgemm_splitk", "mi_sgemm_splitk_workspace_bytes",
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
-    "mi_sgemm_splitk_atomic",
-    "sgemm", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace",
+    "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
+    "mi_reduce_sum_max_additions",
+    "sgemm", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace", "reduce_sum",
     "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "KERNEL_SPLITK_ATOMIC", "EXPORTED_SYMBOLS",
 ]
 
@@ -44,7 +45,8 @@ EXPORTED_SYMBOLS = (
     "mi_sgemm", "mi_sgemm_valu", "mi_sgemm_splitk_workspace_bytes", "mi_sgemm_splitk",
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
-    "mi_sgemm_splitk_atomic",
+    "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
+    "mi_reduce_sum_max_additions",
 )
 
 if not LIB_PATH.exists():
@@ -101,6 +103,12 @@ lib.mi_sgemm_splitk_with_config_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.mi_sgemm_splitk_with_config_workspace_bytes.restype = _sz
 lib.mi_sgemm_splitk_atomic.argtypes = _GEMM_ARGS + [_i, _vp]
 lib.mi_sgemm_splitk_atomic.restype = _i
+lib.mi_reduce_sum.argtypes = [ctypes.c_longlong, _vp, _vp, _vp, _sz, _vp]
+lib.mi_reduce_sum.restype = _i
+lib.mi_reduce_sum_workspace_bytes.argtypes = [ctypes.c_longlong]
+lib.mi_reduce_sum_workspace_bytes.restype = _sz
+lib.mi_reduce_sum_max_additions.argtypes = [ctypes.c_longlong]
+lib.mi_reduce_sum_max_additions.restype = ctypes.c_longlong
 lib.mi_status_string.argtypes = [_i]
 lib.mi_status_string.restype = ctypes.c_char_p
 lib.mi_sgemm_get_plan.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(Plan)]
@@ -156,6 +164,18 @@ def mi_sgemm_splitk_atomic(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits=
                            stream=None) -> int:
     return lib.mi_sgemm_splitk_atomic(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits,
                                       stream)
+
+
+def mi_reduce_sum(n, x, out, ws, ws_bytes, stream=None) -> int:
+    return lib.mi_reduce_sum(n, x, out, ws, ws_bytes, stream)
+
+
+def mi_reduce_sum_workspace_bytes(n) -> int:
+    return lib.mi_reduce_sum_workspace_bytes(n)
+
+
+def mi_reduce_sum_max_additions(n) -> int:
+    return lib.mi_reduce_sum_max_additions(n)
 
 
 def mi_status_string(status: int) -> str:
@@ -284,3 +304,25 @@ def sgemm_splitk_atomic(A, B, C=None, alpha=1.0, beta=0.0, splits=0, stream=None
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_splitk_atomic")
     return C
+
+
+def reduce_sum(x, out=None, workspace=None, stream=None):
+    """Sum of a 1-D float32 device tensor (contiguous); returns a 1-element
+    device tensor."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or not x.is_cuda:
+        raise TypeError("x must be a float32 device tensor")
+    if x.dim() != 1 or (x.numel() > 1 and x.stride(0) != 1):
+        raise ValueError("x must be 1-D and contiguous")
+    n = x.numel()
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(mi_reduce_sum_workspace_bytes(n), 4), dtype=torch.uint8,
+                                device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mi_reduce_sum(n, x.data_ptr() if n else None, out.data_ptr(), workspace.data_ptr(),
+                           ws_bytes, _stream(stream))
+    if st != SUCCESS:
+        raise MiSgemmError(st, "mi_reduce_sum")
+    return out

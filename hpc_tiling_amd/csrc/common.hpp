@@ -74,4 +74,35 @@ __device__ __forceinline__ f32x4 load4_masked(const float *src, int valid) {
     return v;
 }
 
+// Sum of x over the four lanes {l, l^16, l^32, l^48}, returned in all of them:
+// two butterfly steps with gfx950's row-swap instructions.
+__device__ __forceinline__ float sum_over_lane_quarters(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    // h[0] holds x of lanes (l < 32 ? l : l - 32), h[1] of (l < 32 ? l + 32 : l).
+    const float y = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const unsigned w = __float_as_uint(y);
+    const auto q = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// x rotated right by N lanes within each row of 16 (DPP row_ror:N).
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
+// Sum of x over the whole wave, returned in every lane.  Rotating a row of
+// 16 by 8, 4, 2, 1 and adding leaves the row sum in all its lanes (after the
+// first step the values are symmetric under lane ^ 8, so a rotation by 4
+// pairs each lane with lane ^ 4, and so on); the row-swap butterflies then
+// add the four rows.  6 addition levels; the order is fixed.
+__device__ __forceinline__ float wave_sum(float x) {
+    x += row_ror<8>(x);
+    x += row_ror<4>(x);
+    x += row_ror<2>(x);
+    x += row_ror<1>(x);
+    return sum_over_lane_quarters(x);
+}
+
 }  // namespace mi

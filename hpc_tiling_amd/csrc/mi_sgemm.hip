@@ -11,6 +11,7 @@
 #include "mi_sgemm.h"
 #include "sgemm_mfma.hpp"
 #include "sgemm_valu.hpp"
+#include "reduce.hpp"
 #include "splitk.hpp"
 
 namespace mi {
@@ -341,6 +342,16 @@ int run_splitk_atomic(int config, int m, int n, int k, float alpha, const float 
                   64 * c.wgm * c.wgn, s, a);
 }
 
+// ---------------------------------------------------------------------------
+// Array sum.
+// ---------------------------------------------------------------------------
+// Partial-pass grid: at least 64 inputs per lane, at most 4 workgroups per CU.
+long long reduce_grid(long long n) {
+    long long g = ceil_div(n, (long long)kReduceThreads * 64);
+    if (g > 4 * kCUs) g = 4 * kCUs;
+    return g < 1 ? 1 : g;
+}
+
 }  // namespace
 }  // namespace mi
 
@@ -397,6 +408,46 @@ size_t mi_sgemm_splitk_with_config_workspace_bytes(int config, int m, int n, int
         return 0;
     const int id = config < 0 ? choose_split_config(m, n, k) : config;
     return plan_split(m, n, k, splits, id).bytes;
+}
+
+size_t mi_reduce_sum_workspace_bytes(long long n) {
+    if (n <= 0) return 0;
+    return (size_t)reduce_grid(n) * sizeof(float);
+}
+
+long long mi_reduce_sum_max_additions(long long n) {
+    if (n <= 0) return 0;
+    const long long g = reduce_grid(n);
+    const long long per_acc = ceil_div(ceil_div(n, 4), g * kReduceThreads);  // float4s per lane
+    // per accumulator (+1 for a trailing element), 2 levels over the four
+    // accumulators, 6 in the wave, 2 over the waves; then the final pass:
+    // ceil(g / 256) in a lane, 6 + 2 levels.
+    return per_acc + 1 + 2 + 6 + 2 + ceil_div(g, kReduceThreads) + 6 + 2;
+}
+
+int mi_reduce_sum(long long n, const float *x, float *out, void *ws, size_t ws_bytes,
+                  void *stream) {
+    if (n < 0) return MI_SGEMM_ERROR_INVALID_VALUE;
+    if (!out || (n > 0 && !x)) return MI_SGEMM_ERROR_NULL_POINTER;
+    const long long g = n > 0 ? reduce_grid(n) : 0;
+    if (g > 0 && (!ws || ws_bytes < (size_t)g * sizeof(float))) return MI_SGEMM_ERROR_WORKSPACE;
+    int st = check_device();
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *partials = static_cast<float *>(ws);
+    if (g > 0) {
+        const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+        void *args[] = {&x, &n, &partials};
+        st = launch_raw(vec ? reinterpret_cast<const void *>(&reduce_partial_kernel<true>)
+                            : reinterpret_cast<const void *>(&reduce_partial_kernel<false>),
+                        g, kReduceThreads, args, s);
+        if (st) return st;
+    }
+    int count = (int)g;
+    const float *pc = partials;
+    void *args[] = {&pc, &count, &out};
+    return launch_raw(reinterpret_cast<const void *>(&reduce_final_kernel), 1, kReduceThreads,
+                      args, s);
 }
 
 const char *mi_status_string(int status) {

@@ -1,0 +1,64 @@
+// reduce.hpp -- sum of a float array (page aerisun.top, section
+// "Reduce 的分层归约"): every lane first accumulates many inputs in registers
+// (grid-stride loop, section "先在线程内累加，再交换部分和"), then the wave
+// adds its lanes with register exchanges instead of LDS (section
+// "Warp shuffle 的数据交换", on wave64 with DPP rotations and row swaps), the
+// four waves of a workgroup meet in LDS, and a second single-workgroup kernel
+// adds the per-workgroup partials -- two passes and no atomics, so the
+// result is the same bits on every run.
+#pragma once
+
+#include "common.hpp"
+
+namespace mi {
+
+constexpr int kReduceThreads = 256;
+
+// Workgroup partial sums.  VEC: x is 16-byte aligned (float4 loads; the last
+// n % 4 elements are added by the first threads).  Each lane keeps four
+// accumulators (one per float4 component) and adds one float4 per stride,
+// unrolled four deep for loads in flight.
+template <bool VEC>
+__global__ __launch_bounds__(kReduceThreads) void reduce_partial_kernel(const float *__restrict__ x,
+                                                                      long long n,
+                                                                      float *__restrict__ partials) {
+    const long long tid = (long long)blockIdx.x * kReduceThreads + threadIdx.x;
+    const long long stride = (long long)gridDim.x * kReduceThreads;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (VEC) {
+        const f32x4 *xv = reinterpret_cast<const f32x4 *>(x);
+        const long long nv = n >> 2;
+        long long i = tid;
+        for (; i + 3 * stride < nv; i += 4 * stride) {
+            const f32x4 a = xv[i], b = xv[i + stride], c = xv[i + 2 * stride], d = xv[i + 3 * stride];
+            acc += a;
+            acc += b;
+            acc += c;
+            acc += d;
+        }
+        for (; i < nv; i += stride) acc += xv[i];
+        const long long rest = n - 4 * nv;  // 0..3 trailing elements
+        if (tid < rest) acc[0] += x[4 * nv + tid];
+    } else {
+        for (long long i = tid; i < n; i += stride) acc[0] += x[i];
+    }
+    float s = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    __shared__ float wave_part[kReduceThreads / 64];
+    if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) partials[blockIdx.x] = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
+}
+
+// out[0] = sum of the `count` partials (count may be 0), one workgroup.
+__global__ __launch_bounds__(kReduceThreads) void reduce_final_kernel(const float *__restrict__ partials,
+                                                                    int count, float *out) {
+    float s = 0.f;
+    for (int i = threadIdx.x; i < count; i += kReduceThreads) s += partials[i];
+    s = wave_sum(s);
+    __shared__ float wave_part[kReduceThreads / 64];
+    if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) out[0] = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
+}
+
+}  // namespace mi

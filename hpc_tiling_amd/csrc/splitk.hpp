@@ -24,17 +24,6 @@
 
 namespace mi {
 
-// Sum of x over the four lanes {l, l^16, l^32, l^48}, returned in all of them.
-__device__ __forceinline__ float sum_over_lane_quarters(float x) {
-    const unsigned u = __float_as_uint(x);
-    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    // h[0] holds x of lanes (l < 32 ? l : l - 32), h[1] of (l < 32 ? l + 32 : l).
-    const float y = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    const unsigned w = __float_as_uint(y);
-    const auto q = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
 __global__ __launch_bounds__(256) void splitk_combine_kernel(const float *__restrict__ ws,
                                                              long long ws_slice, int splits,
                                                              int m, int n, float alpha,

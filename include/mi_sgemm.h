@@ -134,6 +134,33 @@ int mi_sgemm_splitk_atomic(int m, int n, int k, float alpha,
                            const float *A, int lda, const float *B, int ldb,
                            float beta, float *C, int ldc, int splits, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Sum of a float array.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * mi_reduce_sum -- out[0] = sum_{i<n} x[i] (page aerisun.top, section
+ * "Reduce 的分层归约"): lanes accumulate many inputs in registers, waves add
+ * their lanes with cross-lane operations (DPP row rotations and row swaps),
+ * workgroups meet in LDS, and a second pass adds the workgroup partials; no
+ * atomics, so the result is the same bits on every run.  x: n floats of
+ * device memory (any 4-byte alignment; 16-byte aligned is faster); out: one
+ * float of device memory, written (0 when n == 0); ws / ws_bytes: device
+ * workspace of at least mi_reduce_sum_workspace_bytes(n) bytes.  Errors:
+ * INVALID_VALUE (n < 0), NULL_POINTER, WORKSPACE, LAUNCH, DEVICE.
+ */
+int mi_reduce_sum(long long n, const float *x, float *out, void *ws, size_t ws_bytes,
+                  void *stream);
+size_t mi_reduce_sum_workspace_bytes(long long n);
+
+/*
+ * mi_reduce_sum_max_additions -- the largest number of floating-point
+ * additions any input passes through on its way to out[0] for this n.  With
+ * u = 2^-24, |computed - exact| <= max_additions * u * sum_i |x_i| (to first
+ * order), which is the error bound of mi_reduce_sum.
+ */
+long long mi_reduce_sum_max_additions(long long n);
+
 /* Text for a mi_status value (a static string; never NULL). */
 const char *mi_status_string(int status);
 

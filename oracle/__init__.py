@@ -24,6 +24,7 @@ import numpy as np
 
 HERE = Path(__file__).resolve().parent
 SRC = HERE / "oracle_sgemm.c"
+SRC_REDUCE = HERE / "oracle_reduce.c"
 LIB = HERE / "liboracle_sgemm.so"
 
 _i64 = ctypes.c_int64
@@ -31,12 +32,14 @@ _f32 = ctypes.c_float
 _vp = ctypes.c_void_p
 
 
-def build(src: Path | str = SRC, out: Path | str = LIB) -> Path:
-    """Compile the oracle with gcc into a shared library (always rebuilds)."""
+def build(src: Path | str = SRC, out: Path | str = LIB,
+          src_reduce: Path | str = SRC_REDUCE) -> Path:
+    """Compile the oracle (GEMM and array-sum sources) with gcc into a shared
+    library (always rebuilds)."""
     out = Path(out)
     tmp = out.with_name(out.name + f".tmp{os.getpid()}")
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-           str(src), "-o", str(tmp), "-lm"]
+           str(src), str(src_reduce), "-o", str(tmp), "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -79,6 +82,8 @@ class Oracle:
         lib.oracle_sgemm.argtypes = [
             _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
             _vp, _vp, ctypes.c_int]
+        lib.oracle_sum.restype = ctypes.c_int
+        lib.oracle_sum.argtypes = [_i64, _vp, _vp, _vp]
         lib.oracle_sgemm_points.restype = ctypes.c_int
         lib.oracle_sgemm_points.argtypes = [
             _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
@@ -111,6 +116,17 @@ class Oracle:
             raise ValueError(f"oracle_sgemm_rows returned {rc}")
         return {"C": Cout.reshape(np.shape(C)) if np.ndim(C) == 2 else Cout,
                 "S": S, "G": G}
+
+    # -- sum of an array ------------------------------------------------
+    def sum(self, x):
+        """(sum, sum of absolute values) of a float32 array, in double."""
+        xf = _f32_flat(np.ascontiguousarray(x), "x")
+        s = ctypes.c_double()
+        a = ctypes.c_double()
+        rc = self.lib.oracle_sum(xf.size, _ptr(xf), ctypes.byref(s), ctypes.byref(a))
+        if rc != 0:
+            raise ValueError(f"oracle_sum returned {rc}")
+        return s.value, a.value
 
     # -- single entries -------------------------------------------------
     def points(self, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ii, jj):

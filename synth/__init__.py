@@ -152,3 +152,23 @@ def sample_rows(seed, m: int, count: int) -> np.ndarray:
     if count > 1:
         pick[-1] = m - 1
     return np.unique(pick)
+
+
+# Array-sum workloads (the reduction of page aerisun.top, section
+# "Reduce 的分层归约"): n float32 values, uniform on [-1, 1).
+REDUCE_WORKLOADS = {
+    "reduce_sum_1048576": (200, 1 << 20),
+    "reduce_sum_268435456": (201, 1 << 28),
+}
+
+
+def vector(name_or_n, integer_twin: bool = False, seed_id: int | None = None) -> np.ndarray:
+    """The seeded input of a named array-sum workload, or of size n (with
+    seed id `seed_id`, default 299)."""
+    if isinstance(name_or_n, str):
+        wid, n = REDUCE_WORKLOADS[name_or_n]
+    else:
+        wid, n = (299 if seed_id is None else seed_id), int(name_or_n)
+    seed = [wid, 0, 1] if integer_twin else [wid, 0]
+    rng = np.random.default_rng(seed)
+    return draw(rng, 1, n, "int3" if integer_twin else "uniform").reshape(n)

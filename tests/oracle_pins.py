@@ -335,6 +335,45 @@ ALL_PINS = [
 ]
 
 
+# --------------------------------------------------------------------------
+# array sum (oracle_sum)
+# --------------------------------------------------------------------------
+def pin_sum_arith_series(orc):
+    for n in (0, 1, 2, 7, 1000, 1 << 20):
+        x = np.arange(1, n + 1, dtype=np.float32)
+        s, a = orc.sum(x)
+        assert s == n * (n + 1) // 2 and a == s, n
+
+
+def pin_sum_integers(orc):
+    rng = np.random.default_rng(43)
+    for n in (5, 4097, 300001):
+        xi = rng.integers(-3, 4, n).astype(np.int64)
+        s, a = orc.sum(xi.astype(np.float32))
+        assert s == xi.sum() and a == np.abs(xi).sum(), n
+
+
+def pin_sum_exact_rational(orc):
+    import math
+    rng = np.random.default_rng(47)
+    for n in (1, 3, 64, 1001):
+        x = rng.standard_normal(n).astype(np.float32) * np.float32(1e3)
+        s, a = orc.sum(x)
+        exact = math.fsum(float(v) for v in x)           # correctly rounded
+        aexact = math.fsum(abs(float(v)) for v in x)
+        assert abs(s - exact) <= n * 2.0 ** -53 * aexact + abs(exact) * 2.0 ** -53, n
+        assert abs(a - aexact) <= n * 2.0 ** -53 * aexact, n
+
+
+def pin_sum_cancellation(orc):
+    x = np.array([1e8, 1.0, -1e8, 0.5, 3.0, -0.25], dtype=np.float32)
+    s, a = orc.sum(x)
+    assert s == 4.25 and a == 2e8 + 4.75
+
+
+ALL_PINS += [pin_sum_arith_series, pin_sum_integers, pin_sum_exact_rational, pin_sum_cancellation]
+
+
 def main(argv):
     """Run every pin against the oracle library named on the command line.
     Exit status 0 when all pass, 1 when any fails (names printed)."""

@@ -162,3 +162,20 @@ def test_valid_call_without_gpu_reports_no_device():
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present; this checks the no-device path")
     assert hta.mi_sgemm(4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4) == hta.ERROR_DEVICE
+
+
+def test_reduce_sum_argument_errors_and_queries():
+    E = hta
+    assert hta.mi_reduce_sum(-1, P, P, P, 4) == E.ERROR_INVALID_VALUE
+    assert hta.mi_reduce_sum(10, None, P, P, 4) == E.ERROR_NULL_POINTER
+    assert hta.mi_reduce_sum(10, P, None, P, 4) == E.ERROR_NULL_POINTER
+    ws = hta.mi_reduce_sum_workspace_bytes(1 << 20)
+    assert ws >= 4 and ws % 4 == 0
+    assert hta.mi_reduce_sum(1 << 20, P, P, P, ws - 4) == E.ERROR_WORKSPACE
+    assert hta.mi_reduce_sum(1 << 20, P, P, None, ws) == E.ERROR_WORKSPACE
+    assert hta.mi_reduce_sum_workspace_bytes(0) == 0
+    # the stated error bound grows with the work per lane and stays small
+    assert hta.mi_reduce_sum_max_additions(0) == 0
+    d1 = hta.mi_reduce_sum_max_additions(1)
+    dbig = hta.mi_reduce_sum_max_additions(1 << 28)
+    assert 0 < d1 <= dbig < 400

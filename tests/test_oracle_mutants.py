@@ -48,6 +48,32 @@ MUTANTS = [
 ]
 
 
+# mistakes planted in oracle_reduce.c
+MUTANTS_REDUCE = [
+    ("sum_drop_last", "for (int64_t i = 0; i < n; ++i)", "for (int64_t i = 0; i + 1 < n; ++i)"),
+    ("sum_drop_first", "for (int64_t i = 0; i < n; ++i)", "for (int64_t i = 1; i < n; ++i)"),
+    ("sum_float_acc", "        s += v;", "        s = (float)(s + v);"),
+    ("sum_abs_signed", "a += fabs(v);", "a += v;"),
+    ("sum_sign", "        s += v;", "        s -= v;"),
+]
+
+
+def _run_pins_on(tmp_path, sgemm_src, reduce_src):
+    lib = oracle.build(sgemm_src, tmp_path / "liboracle_mutant.so", reduce_src)
+    return subprocess.run([sys.executable, str(PINS), str(lib)], cwd=ROOT,
+                          capture_output=True, text=True, timeout=300)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS_REDUCE, ids=[m[0] for m in MUTANTS_REDUCE])
+def test_reduce_mutant_is_caught(tmp_path, name, old, new):
+    src = oracle.SRC_REDUCE.read_text()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    mutated = tmp_path / "oracle_reduce_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    res = _run_pins_on(tmp_path, oracle.SRC, mutated)
+    assert res.returncode != 0, f"mutant {name} passed every pin:\n{res.stdout}"
+
+
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(tmp_path, name, old, new):
     src = oracle.SRC.read_text()
