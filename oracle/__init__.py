@@ -11,7 +11,9 @@ compiles that file with gcc and marshals numpy arrays to it.
 
 All functions take the operands as flat or 2-D C-contiguous float32 numpy
 arrays in row-major storage with an explicit leading dimension, mirroring the
-C interface: A_it = A[i*lda + t], B_tj = B[t*ldb + j], C_ij = C[i*ldc + j].
+C interface: A_it = A[i*lda + t], B_tj = B[t*ldb + j], C_ij = C[i*ldc + j];
+with ``trans_a`` / ``trans_b`` an operand is stored transposed instead:
+A_it = A[t*lda + i] (A is k x m), B_tj = B[j*ldb + t] (B is n x k).
 """
 from __future__ import annotations
 
@@ -78,6 +80,9 @@ class Oracle:
         lib.oracle_sgemm_rows.argtypes = [
             _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
             _i64, _vp, _vp, _vp, ctypes.c_int]
+        lib.oracle_sgemm_rows_ex.restype = ctypes.c_int
+        lib.oracle_sgemm_rows_ex.argtypes = [ctypes.c_int, ctypes.c_int] + list(
+            lib.oracle_sgemm_rows.argtypes)
         lib.oracle_sgemm.restype = ctypes.c_int
         lib.oracle_sgemm.argtypes = [
             _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
@@ -88,11 +93,15 @@ class Oracle:
         lib.oracle_sgemm_points.argtypes = [
             _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
             _i64, _vp, _vp, _vp, _vp, _vp]
+        lib.oracle_sgemm_points_ex.restype = ctypes.c_int
+        lib.oracle_sgemm_points_ex.argtypes = [ctypes.c_int, ctypes.c_int] + list(
+            lib.oracle_sgemm_points.argtypes)
         self.lib = lib
 
     # -- whole matrix / selected rows ------------------------------------
     def sgemm(self, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, *,
-              rows=None, want_s=False, want_g=False, threads=None):
+              rows=None, want_s=False, want_g=False, threads=None,
+              trans_a=False, trans_b=False):
         """Returns dict(C=updated copy of C, S=..., G=...).
 
         With ``rows`` (a sequence of row indices) only those rows of the
@@ -109,7 +118,8 @@ class Oracle:
         S = np.empty((nrows, n), dtype=np.float64) if want_s else None
         G = np.empty((nrows, n), dtype=np.float64) if want_g else None
         t = default_threads() if threads is None else int(threads)
-        rc = self.lib.oracle_sgemm_rows(
+        rc = self.lib.oracle_sgemm_rows_ex(
+            int(bool(trans_a)), int(bool(trans_b)),
             m, n, k, alpha, _ptr(Af), lda, _ptr(Bf), ldb, beta, _ptr(Cout), ldc,
             nrows, _ptr(rows_arr), _ptr(S), _ptr(G), t)
         if rc != 0:
@@ -129,7 +139,8 @@ class Oracle:
         return s.value, a.value
 
     # -- single entries -------------------------------------------------
-    def points(self, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ii, jj):
+    def points(self, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ii, jj, *,
+               trans_a=False, trans_b=False):
         """Entries (ii[p], jj[p]); returns dict(C=float32[p], S=..., G=...)."""
         Af = _f32_flat(np.ascontiguousarray(A), "A")
         Bf = _f32_flat(np.ascontiguousarray(B), "B")
@@ -143,7 +154,8 @@ class Oracle:
         G = np.empty(ii.size, dtype=np.float64)
         if Cf is None and beta != 0:
             raise ValueError("beta != 0 needs C")
-        rc = self.lib.oracle_sgemm_points(
+        rc = self.lib.oracle_sgemm_points_ex(
+            int(bool(trans_a)), int(bool(trans_b)),
             m, n, k, alpha, _ptr(Af), lda, _ptr(Bf), ldb, beta, _ptr(Cf), ldc,
             ii.size, _ptr(ii), _ptr(jj), _ptr(out), _ptr(S), _ptr(G))
         if rc != 0:

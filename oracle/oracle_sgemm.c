@@ -20,6 +20,13 @@
  * 复用", which assigns adjacent threads to adjacent columns of a row-major
  * operand) with a leading dimension per matrix:
  *     A_it = A[i*lda + t],  B_tj = B[t*ldb + j],  C_ij = C[i*ldc + j].
+ * The _ex forms also take either operand stored transposed (the BLAS
+ * op(X) = X^T; page "GEMM优化原理", section 基于 register 计算, discusses
+ * reading an operand in transposed order):
+ *     trans_a = 1:  A_it = A[t*lda + i]   (A stored k x m, lda >= m)
+ *     trans_b = 1:  B_tj = B[j*ldb + t]   (B stored n x k, ldb >= k)
+ * which is the same sum with other element addresses: the code below reads
+ * A_it at A[i*sa_i + t*sa_t] and B_tj at B[t*sb_t + j*sb_j].
  *
  * How it is computed (nothing beyond the definition)
  * ---------------------------------------------------
@@ -51,7 +58,9 @@ typedef struct {
     int64_t n, k;
     double alpha, beta;
     const float *A, *B;
-    int64_t lda, ldb, ldc;
+    int64_t sa_i, sa_t;    /* A_it = A[i*sa_i + t*sa_t] */
+    int64_t sb_t, sb_j;    /* B_tj = B[t*sb_t + j*sb_j] */
+    int64_t ldc;
     float *C;              /* in/out, row-major with ldc */
     double *S, *G;         /* optional dense outputs, one row per computed row */
     const int64_t *rows;   /* rows to compute, or NULL for 0..nrows-1 */
@@ -68,10 +77,10 @@ static void one_row(const row_job *jb, int64_t slot, int64_t i,
     for (int64_t j = 0; j < n; ++j) { acc[j] = 0.0; gacc[j] = 0.0; }
     if (use_ab) {
         for (int64_t t = 0; t < k; ++t) {
-            const double a = (double)jb->A[i * jb->lda + t];
-            const float *brow = jb->B + t * jb->ldb;
+            const double a = (double)jb->A[i * jb->sa_i + t * jb->sa_t];
+            const float *brow = jb->B + t * jb->sb_t;
             for (int64_t j = 0; j < n; ++j) {
-                const double p = a * (double)brow[j];
+                const double p = a * (double)brow[j * jb->sb_j];
                 acc[j] += p;
                 gacc[j] += fabs(p);
             }
@@ -102,23 +111,33 @@ static void *row_worker(void *arg)
     return NULL;
 }
 
+/* Stored row widths: A is m x k (k x m transposed), B is k x n (n x k). */
+static int bad_ld(int ta, int tb, int64_t m, int64_t n, int64_t k,
+                  int64_t lda, int64_t ldb, int64_t ldc)
+{
+    const int64_t wa = ta ? m : k, wb = tb ? k : n;
+    if ((ta != 0 && ta != 1) || (tb != 0 && tb != 1)) return 1;
+    return lda < (wa > 1 ? wa : 1) || ldb < (wb > 1 ? wb : 1) || ldc < (n > 1 ? n : 1);
+}
+
 /*
- * oracle_sgemm_rows: computes the output rows listed in `rows` (nrows
+ * oracle_sgemm_rows_ex: computes the output rows listed in `rows` (nrows
  * entries, each in [0, m)); rows == NULL means all rows 0..m-1 (nrows = m).
  * C is updated in place at those rows only.  S and G, when not NULL, receive
- * nrows x n dense doubles in the order of `rows`.
+ * nrows x n dense doubles in the order of `rows`.  trans_a / trans_b (0 or 1)
+ * select the stored forms described at the top of this file.
  * Returns 0 on success, -1 on a bad argument, -2 when memory runs out.
  */
-int oracle_sgemm_rows(int64_t m, int64_t n, int64_t k, float alpha,
-                      const float *A, int64_t lda, const float *B, int64_t ldb,
-                      float beta, float *C, int64_t ldc,
-                      int64_t nrows, const int64_t *rows,
-                      double *S, double *G, int nthreads)
+int oracle_sgemm_rows_ex(int trans_a, int trans_b, int64_t m, int64_t n, int64_t k,
+                         float alpha, const float *A, int64_t lda, const float *B, int64_t ldb,
+                         float beta, float *C, int64_t ldc,
+                         int64_t nrows, const int64_t *rows,
+                         double *S, double *G, int nthreads)
 {
     if (m < 0 || n < 0 || k < 0 || nrows < 0) return -1;
     if (!rows && nrows != m) return -1;
     if (nrows == 0 || n == 0) return 0;
-    if (lda < (k > 1 ? k : 1) || ldb < (n > 1 ? n : 1) || ldc < (n > 1 ? n : 1)) return -1;
+    if (bad_ld(trans_a, trans_b, m, n, k, lda, ldb, ldc)) return -1;
     if (rows)
         for (int64_t s = 0; s < nrows; ++s)
             if (rows[s] < 0 || rows[s] >= m) return -1;
@@ -133,7 +152,11 @@ int oracle_sgemm_rows(int64_t m, int64_t n, int64_t k, float alpha,
         row_job *jb = &jobs[w];
         jb->n = n; jb->k = k;
         jb->alpha = (double)alpha; jb->beta = (double)beta;
-        jb->A = A; jb->B = B; jb->lda = lda; jb->ldb = ldb; jb->ldc = ldc;
+        jb->A = A; jb->B = B; jb->ldc = ldc;
+        jb->sa_i = trans_a ? 1 : lda;
+        jb->sa_t = trans_a ? lda : 1;
+        jb->sb_t = trans_b ? 1 : ldb;
+        jb->sb_j = trans_b ? ldb : 1;
         jb->C = C; jb->S = S; jb->G = G; jb->rows = rows;
         jb->row_begin = nrows * w / nthreads;
         jb->row_end = nrows * (w + 1) / nthreads;
@@ -153,30 +176,43 @@ int oracle_sgemm_rows(int64_t m, int64_t n, int64_t k, float alpha,
     return rc;
 }
 
+/* Operands as given (row-major A and B). */
+int oracle_sgemm_rows(int64_t m, int64_t n, int64_t k, float alpha,
+                      const float *A, int64_t lda, const float *B, int64_t ldb,
+                      float beta, float *C, int64_t ldc,
+                      int64_t nrows, const int64_t *rows,
+                      double *S, double *G, int nthreads)
+{
+    return oracle_sgemm_rows_ex(0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                                nrows, rows, S, G, nthreads);
+}
+
 /* Whole-matrix form: every row of C. */
 int oracle_sgemm(int64_t m, int64_t n, int64_t k, float alpha,
                  const float *A, int64_t lda, const float *B, int64_t ldb,
                  float beta, float *C, int64_t ldc,
                  double *S, double *G, int nthreads)
 {
-    return oracle_sgemm_rows(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
-                             m, NULL, S, G, nthreads);
+    return oracle_sgemm_rows_ex(0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                                m, NULL, S, G, nthreads);
 }
 
 /*
- * oracle_sgemm_points: single entries (ii[p], jj[p]) for p < npts, computed
- * as a dot product over ascending t -- the same sum, in the same order, as
- * the row form.  Results go to out[p] (float), S[p] and G[p] (optional); C is
- * only read (when beta != 0).
+ * oracle_sgemm_points_ex: single entries (ii[p], jj[p]) for p < npts,
+ * computed as a dot product over ascending t -- the same sum, in the same
+ * order, as the row form.  Results go to out[p] (float), S[p] and G[p]
+ * (optional); C is only read (when beta != 0).
  */
-int oracle_sgemm_points(int64_t m, int64_t n, int64_t k, float alpha,
-                        const float *A, int64_t lda, const float *B, int64_t ldb,
-                        float beta, const float *C, int64_t ldc,
-                        int64_t npts, const int64_t *ii, const int64_t *jj,
-                        float *out, double *S, double *G)
+int oracle_sgemm_points_ex(int trans_a, int trans_b, int64_t m, int64_t n, int64_t k,
+                           float alpha, const float *A, int64_t lda, const float *B, int64_t ldb,
+                           float beta, const float *C, int64_t ldc,
+                           int64_t npts, const int64_t *ii, const int64_t *jj,
+                           float *out, double *S, double *G)
 {
     if (m < 0 || n < 0 || k < 0 || npts < 0) return -1;
-    if (lda < (k > 1 ? k : 1) || ldb < (n > 1 ? n : 1) || ldc < (n > 1 ? n : 1)) return -1;
+    if (bad_ld(trans_a, trans_b, m, n, k, lda, ldb, ldc)) return -1;
+    const int64_t sa_i = trans_a ? 1 : lda, sa_t = trans_a ? lda : 1;
+    const int64_t sb_t = trans_b ? 1 : ldb, sb_j = trans_b ? ldb : 1;
     const double da = (double)alpha, db = (double)beta;
     const int use_ab = (k > 0 && alpha != 0.0f);
     for (int64_t p = 0; p < npts; ++p) {
@@ -185,7 +221,7 @@ int oracle_sgemm_points(int64_t m, int64_t n, int64_t k, float alpha,
         double s = 0.0, g = 0.0;
         if (use_ab) {
             for (int64_t t = 0; t < k; ++t) {
-                const double prod = (double)A[i * lda + t] * (double)B[t * ldb + j];
+                const double prod = (double)A[i * sa_i + t * sa_t] * (double)B[t * sb_t + j * sb_j];
                 s += prod;
                 g += fabs(prod);
             }
@@ -197,4 +233,15 @@ int oracle_sgemm_points(int64_t m, int64_t n, int64_t k, float alpha,
         if (G) G[p] = g;
     }
     return 0;
+}
+
+/* Operands as given (row-major A and B). */
+int oracle_sgemm_points(int64_t m, int64_t n, int64_t k, float alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb,
+                        float beta, const float *C, int64_t ldc,
+                        int64_t npts, const int64_t *ii, const int64_t *jj,
+                        float *out, double *S, double *G)
+{
+    return oracle_sgemm_points_ex(0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                                  npts, ii, jj, out, S, G);
 }

@@ -132,6 +132,36 @@ def operands(w: Workload, integer_twin: bool = False):
     return A, B, C
 
 
+def transposed_storage(M: np.ndarray, cols: int, ld: int, pad=np.float32(np.nan)) -> np.ndarray:
+    """Storage of the transpose of the logical block M[:, :cols]: a
+    cols x ld array (ld >= M's row count), pads set to `pad`."""
+    return padded(np.ascontiguousarray(M[:, :cols].T), ld, pad)
+
+
+def transposed_ld(rows: int, width: int, ld: int) -> int:
+    """Leading dimension for storing a rows-long operand transposed, keeping
+    the padding of the as-given layout (ld - width) and, when ld is a
+    multiple of 4, that property too."""
+    out = rows + (ld - width)
+    if ld % 4 == 0:
+        out = (out + 3) // 4 * 4
+    return max(out, 1)
+
+
+def operands_ex(w: Workload, trans_a: bool, trans_b: bool, integer_twin: bool = False):
+    """(A, lda, B, ldb, C) with the values of operands(w); A is stored k x m
+    when trans_a, B is stored n x k when trans_b (NaN pads)."""
+    A, B, C = operands(w, integer_twin)
+    lda, ldb = w.lda, w.ldb
+    if trans_a:
+        lda = transposed_ld(w.m, w.k, w.lda)
+        A = transposed_storage(A, w.k, lda)
+    if trans_b:
+        ldb = transposed_ld(w.k, w.n, w.ldb)
+        B = transposed_storage(B, w.n, ldb)
+    return A, lda, B, ldb, C
+
+
 def sample_indices(seed, m: int, n: int, count: int):
     """`count` distinct-ish (i, j) positions for sampled checks, always
     including the four corners of the m x n output."""
@@ -145,8 +175,9 @@ def sample_indices(seed, m: int, n: int, count: int):
 
 def sample_rows(seed, m: int, count: int) -> np.ndarray:
     """`count` distinct rows of an m-row output, always including 0 and m-1."""
+    if count >= m:
+        return np.arange(m, dtype=np.int64)
     rng = np.random.default_rng(seed)
-    count = min(count, m)
     pick = rng.choice(m, size=count, replace=False).astype(np.int64)
     pick[0] = 0
     if count > 1:

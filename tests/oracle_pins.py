@@ -326,12 +326,105 @@ def pin_points(orc):
     assert np.array_equal(p["S"], full["S"][ii, jj]), "points vs rows: same ascending sum"
 
 
+# --------------------------------------------------------------------------
+# operands stored transposed (trans_a: A is k x m; trans_b: B is n x k)
+# --------------------------------------------------------------------------
+def _stored(X, trans, pad_cols):
+    """Storage of logical operand X: X itself or its transpose, padded."""
+    S = np.ascontiguousarray(X.T) if trans else np.asarray(X)
+    return _pad(S, S.shape[1] + pad_cols)
+
+
+def _run_t(orc, Av, Bv, ta, tb, Cin=None, alpha=1.0, beta=0.0, **kw):
+    m, k = Av.shape
+    n = Bv.shape[1]
+    A, B = _stored(Av, ta, 3), _stored(Bv, tb, 5)
+    C = _pad(np.zeros((m, n), np.float32) if Cin is None else Cin, n + 2, SENT)
+    return orc.sgemm(m, n, k, alpha, A, A.shape[1], B, B.shape[1], beta, C, n + 2,
+                     trans_a=ta, trans_b=tb, **kw)
+
+
+def pin_transposed_closed_form(orc):
+    """A_it = i + 1 and B_tj = t give C_ij = (i + 1) k (k - 1) / 2; A_it = t and
+    B_tj = j + 1 give (j + 1) k (k - 1) / 2 -- for every storage order, with
+    NaN pads, so a stored operand read with the wrong strides shows."""
+    m, n, k = 7, 5, 9
+    i = np.arange(m, dtype=np.float32)[:, None]
+    j = np.arange(n, dtype=np.float32)[None, :]
+    t_row = np.arange(k, dtype=np.float32)
+    tri = k * (k - 1) / 2
+    for ta in (False, True):
+        for tb in (False, True):
+            A1 = np.repeat(i + 1, k, axis=1)
+            B1 = np.repeat(t_row[:, None], n, axis=1)
+            C1 = _logical(_run_t(orc, A1, B1, ta, tb)["C"], m, n)
+            assert np.array_equal(C1, np.repeat((i + 1) * tri, n, axis=1)), (ta, tb, "A=i+1")
+            A2 = np.repeat(t_row[None, :], m, axis=0)
+            B2 = np.repeat(j + 1, k, axis=0)
+            C2 = _logical(_run_t(orc, A2, B2, ta, tb)["C"], m, n)
+            assert np.array_equal(C2, np.repeat((j + 1) * tri, m, axis=0)), (ta, tb, "B=j+1")
+
+
+def pin_transposed_integer_exact(orc):
+    """Small integers are summed exactly; numpy int64 matmul of the logical
+    operands is the reference, for all four storage orders."""
+    rng = np.random.default_rng(43)
+    for (m, n, k) in TAIL_SHAPES + [(12, 40, 300)]:
+        Ai = rng.integers(-3, 4, (m, k)).astype(np.int64)
+        Bi = rng.integers(-3, 4, (k, n)).astype(np.int64)
+        Ci = rng.integers(-3, 4, (m, n)).astype(np.int64)
+        want = ((3 * (Ai @ Bi) + Ci) / 2.0).astype(np.float32)
+        for ta in (False, True):
+            for tb in (False, True):
+                r = _run_t(orc, Ai.astype(np.float32), Bi.astype(np.float32), ta, tb,
+                           Cin=Ci.astype(np.float32), alpha=1.5, beta=0.5)
+                assert np.array_equal(_logical(r["C"], m, n), want), (m, n, k, ta, tb)
+                assert np.all(r["C"].reshape(m, -1)[:, n:] == SENT), "C pads written"
+
+
+def pin_transposed_points(orc):
+    rng = np.random.default_rng(47)
+    m, n, k = 21, 34, 77
+    Ai = rng.integers(-3, 4, (m, k)).astype(np.int64)
+    Bi = rng.integers(-3, 4, (k, n)).astype(np.int64)
+    ii = np.array([0, 20, 7, 20, 3], np.int64)
+    jj = np.array([0, 33, 33, 0, 11], np.int64)
+    want = (Ai @ Bi)[ii, jj].astype(np.float32)
+    for ta in (False, True):
+        for tb in (False, True):
+            A, B = _stored(Ai.astype(np.float32), ta, 2), _stored(Bi.astype(np.float32), tb, 1)
+            r = orc.points(m, n, k, 1.0, A, A.shape[1], B, B.shape[1], 0.0, None, n, ii, jj,
+                           trans_a=ta, trans_b=tb)
+            assert np.array_equal(r["C"], want), (ta, tb)
+
+
+def pin_transposed_leading_dims(orc):
+    """Stored widths: lda >= m for A^T (may be < k), ldb >= k for B^T (may be
+    < n); one less is rejected."""
+    m, n, k = 3, 9, 6
+    Av = np.ones((m, k), np.float32)
+    Bv = np.ones((k, n), np.float32)
+    At, Bt = np.ascontiguousarray(Av.T), np.ascontiguousarray(Bv.T)   # k x m, n x k
+    C = np.zeros((m, n), np.float32)
+    r = orc.sgemm(m, n, k, 1.0, At, m, Bt, k, 0.0, C, n, trans_a=True, trans_b=True)
+    assert np.array_equal(r["C"], np.full((m, n), k, np.float32))
+    for bad in [dict(lda=m - 1, ldb=k), dict(lda=m, ldb=k - 1)]:
+        try:
+            orc.sgemm(m, n, k, 1.0, At, bad["lda"], Bt, bad["ldb"], 0.0, C, n,
+                      trans_a=True, trans_b=True)
+        except ValueError:
+            continue
+        raise AssertionError(f"accepted {bad}")
+
+
 ALL_PINS = [
     pin_all_ones, pin_arith_series, pin_row_and_column_index, pin_sum_of_squares,
     pin_identity, pin_permutation, pin_integer_exact, pin_brute_force_fraction,
     pin_numpy_float64, pin_transpose, pin_thread_count, pin_alpha_power_of_two,
     pin_alpha_beta_integers, pin_alpha_zero_and_k_zero, pin_beta_zero_ignores_c,
     pin_pads_untouched, pin_rows_subset, pin_points,
+    pin_transposed_closed_form, pin_transposed_integer_exact, pin_transposed_points,
+    pin_transposed_leading_dims,
 ]
 
 

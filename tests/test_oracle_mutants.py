@@ -20,11 +20,11 @@ MUTANTS = [
     ("drop_first_term", "for (int64_t t = 0; t < k; ++t) {\n            const double a",
      "for (int64_t t = 1; t < k; ++t) {\n            const double a"),
     ("wrong_sign", "acc[j] += p;", "acc[j] -= p;"),
-    ("a_transposed", "jb->A[i * jb->lda + t]", "jb->A[t * jb->lda + i]"),
-    ("b_transposed", "const double p = a * (double)brow[j];",
-     "const double p = a * (double)jb->B[j * jb->ldb + t];"),
-    ("b_row_index_i", "const float *brow = jb->B + t * jb->ldb;",
-     "const float *brow = jb->B + i * jb->ldb;"),
+    ("a_transposed", "jb->A[i * jb->sa_i + t * jb->sa_t]", "jb->A[t * jb->sa_i + i * jb->sa_t]"),
+    ("b_transposed", "const double p = a * (double)brow[j * jb->sb_j];",
+     "const double p = a * (double)jb->B[j * jb->sb_t + t * jb->sb_j];"),
+    ("b_row_index_i", "const float *brow = jb->B + t * jb->sb_t;",
+     "const float *brow = jb->B + i * jb->sb_t;"),
     ("alpha_ignored", "double r = use_ab ? jb->alpha * acc[j] : 0.0;",
      "double r = use_ab ? acc[j] : 0.0;"),
     ("beta_sign", "if (jb->beta != 0.0) r += jb->beta * (double)crow[j];",
@@ -33,16 +33,29 @@ MUTANTS = [
      "r += jb->beta * (double)crow[j];"),
     ("alpha_zero_reads_ab", "const int use_ab = (k > 0 && jb->alpha != 0.0);",
      "const int use_ab = (k > 0);"),
-    ("float_accumulator", "const double p = a * (double)brow[j];",
-     "const double p = (double)(float)(a * (double)brow[j]); acc[j] = (float)acc[j];"),
+    ("float_accumulator", "const double p = a * (double)brow[j * jb->sb_j];",
+     "const double p = (double)(float)(a * (double)brow[j * jb->sb_j]); acc[j] = (float)acc[j];"),
     ("g_signed", "gacc[j] += fabs(p);", "gacc[j] += p;"),
     ("row_list_ignored", "const int64_t i = jb->rows ? jb->rows[s] : s;",
      "const int64_t i = s;"),
     ("points_drop_last", "for (int64_t t = 0; t < k; ++t) {\n                const double prod",
      "for (int64_t t = 0; t + 1 < k; ++t) {\n                const double prod"),
-    ("points_transposed_b", "(double)B[t * ldb + j]", "(double)B[j * ldb + t]"),
+    ("points_transposed_b", "(double)B[t * sb_t + j * sb_j]", "(double)B[j * sb_t + t * sb_j]"),
     ("points_beta_sign", "if (db != 0.0) r += db * (double)C[i * ldc + j];",
      "if (db != 0.0) r -= db * (double)C[i * ldc + j];"),
+    # transposed storage
+    ("trans_a_ignored", "jb->sa_i = trans_a ? 1 : lda;\n        jb->sa_t = trans_a ? lda : 1;",
+     "jb->sa_i = lda;\n        jb->sa_t = 1;"),
+    ("trans_b_ignored", "jb->sb_t = trans_b ? 1 : ldb;\n        jb->sb_j = trans_b ? ldb : 1;",
+     "jb->sb_t = ldb;\n        jb->sb_j = 1;"),
+    ("trans_a_stride_m", "jb->sa_t = trans_a ? lda : 1;", "jb->sa_t = trans_a ? m : 1;"),
+    ("trans_b_stride_n", "jb->sb_j = trans_b ? ldb : 1;", "jb->sb_j = trans_b ? n : 1;"),
+    ("points_trans_b_ignored", "const int64_t sb_t = trans_b ? 1 : ldb, sb_j = trans_b ? ldb : 1;",
+     "const int64_t sb_t = ldb, sb_j = 1;"),
+    ("points_trans_a_ignored", "const int64_t sa_i = trans_a ? 1 : lda, sa_t = trans_a ? lda : 1;",
+     "const int64_t sa_i = lda, sa_t = 1;"),
+    ("trans_width_unchecked", "const int64_t wa = ta ? m : k, wb = tb ? k : n;",
+     "const int64_t wa = k, wb = n;"),
     ("c_pad_written", "for (int64_t j = 0; j < n; ++j) {\n        double r",
      "for (int64_t j = 0; j < jb->ldc; ++j) {\n        double r"),
 ]
