@@ -338,17 +338,19 @@ int run_splitk_atomic(int config, int m, int n, int k, float alpha, const float 
     a.tiles_n = (int)ceil_div(n, c.bn);
     a.k_per_split = sp.k_per_split;
     const long long grid = (long long)a.tiles_m * a.tiles_n * sp.splits;
-    return launch(vector_ok(A, lda, B, ldb) ? c.atomic_vec : c.atomic_scalar, grid,
-                  64 * c.wgm * c.wgn, s, a);
+    return launch(c.atomic[vector_ok(A, lda, B, ldb)], grid, 64 * c.wgm * c.wgn, s, a);
 }
 
 // ---------------------------------------------------------------------------
 // Array sum.
 // ---------------------------------------------------------------------------
-// Partial-pass grid: at least 64 inputs per lane, at most 4 workgroups per CU.
+// Partial-pass grid: at least 16 inputs (one unrolled float4 round) per lane,
+// at most 32 workgroups per CU (four waves of residency): a 1 GiB input then
+// gives each lane 128 inputs, the fastest point of a sweep over 8 to 64
+// workgroups per CU and unroll depths 4 to 16.
 long long reduce_grid(long long n) {
-    long long g = ceil_div(n, (long long)kReduceThreads * 64);
-    if (g > 4 * kCUs) g = 4 * kCUs;
+    long long g = ceil_div(n, (long long)kReduceThreads * 16);
+    if (g > 32 * kCUs) g = 32 * kCUs;
     return g < 1 ? 1 : g;
 }
 
