@@ -79,18 +79,30 @@ def make_step(kind, w, Av, Bv, Cv, ws):
     raise ValueError(kind)
 
 
+# Kind suffixes for operands stored transposed (A^T is k x m, B^T is n x k);
+# the stored matrices are passed as transposed (column-major) views.
+TRANS_SUFFIXES = {"_nt": (False, True), "_tn": (True, False), "_tt": (True, True)}
+
+
 def setup(w, kind):
     import torch
     import hpc_tiling_amd as hta
     import synth
-    A, B, C = synth.operands(w)
+    ta = tb = False
+    for suffix, flags in TRANS_SUFFIXES.items():
+        if kind.endswith(suffix):
+            kind = kind[:-len(suffix)]
+            ta, tb = flags
+    A, _, B, _, C = synth.operands_ex(w, ta, tb)
     dev = torch.device("cuda:0")
     Ad, Bd, Cd = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+    Av = Ad[:, :w.m].t() if ta else Ad[:, :w.k]
+    Bv = Bd[:, :w.k].t() if tb else Bd[:, :w.n]
     ws = None
     if kind == "splitk":
         ws = hta.splitk_workspace(w.m, w.n, w.k, 0, device=dev)
     torch.cuda.synchronize()
-    return (A, B, C), (Ad, Bd, Cd), make_step(kind, w, Ad[:, :w.k], Bd[:, :w.n], Cd[:, :w.n], ws)
+    return (A, B, C), (Ad, Bd, Cd), make_step(kind, w, Av, Bv, Cd[:, :w.n], ws)
 
 
 def time_steps(step, steps, warmup):
@@ -128,16 +140,21 @@ def cpu_baseline(w, host, budget_s):
     nrows = int(min(w.m, max(len(probe), budget_s / max(per_row, 1e-9))))
     nrows = max(threads, (nrows // threads) * threads) if nrows < w.m else w.m
     rows = synth.sample_rows([w.wid, 4321], w.m, nrows)
+    # when every row fits the budget, whole passes are repeated to fill it
+    passes = 1 if nrows < w.m else int(max(1, min(50, budget_s / max(per_row * w.m, 1e-9))))
     t0 = time.perf_counter()
-    orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, rows=rows,
-              want_g=True, threads=threads)
+    for _ in range(passes):
+        orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, rows=rows,
+                  want_g=True, threads=threads)
     dt = time.perf_counter() - t0
     used = int(min(threads, len(rows)))
-    flops = 2.0 * len(rows) * w.n * w.k
+    flops = 2.0 * passes * len(rows) * w.n * w.k
+    what = (f"{len(rows)} of {w.m} output rows" if len(rows) < w.m
+            else f"all {w.m} output rows, {passes} pass(es)")
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
-        "sample": (f"{len(rows)} of {w.m} output rows of {w.name} (all {w.n} columns, full k="
-                   f"{w.k}); FP64 accumulation, also summing |A_it B_tj|; {dt:.2f} s"),
+        "sample": (f"{what} of {w.name} (all {w.n} columns, full k={w.k}); FP64 "
+                   f"accumulation, also summing |A_it B_tj|; {dt:.2f} s"),
         "seconds": dt, "cpu": _cpu_model(),
     }
 
@@ -203,7 +220,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--kernel", default="mfma",
-                    help="mfma | valu | splitk | splitk_atomic | mfma_cfgN")
+                    help="mfma | valu | splitk | splitk_atomic | mfma_cfgN; mfma and splitk "
+                         "take a suffix _nt, _tn or _tt for operands stored transposed")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -288,12 +306,17 @@ def main(argv=None):
         pairs = [("mfma", "sgemm_8192x8192x8192_ab"), ("mfma", "sgemm_tails_3001x4997x1023"),
                  ("splitk", "sgemm_splitk_512x512x262144"),
                  ("splitk_atomic", "sgemm_splitk_512x512x262144"), ("valu", "sgemm_2048x2048x2048"),
-                 ("mfma", "sgemm_256x256x256")]
+                 ("mfma", "sgemm_256x256x256"),
+                 ("mfma_nt", "sgemm_2048x2048x2048"), ("mfma_tn", "sgemm_2048x2048x2048"),
+                 ("mfma_tt", "sgemm_2048x2048x2048"), ("mfma_tt", "sgemm_8192x8192x8192_ab"),
+                 ("splitk_tn", "sgemm_splitk_512x512x262144")]
         line["secondary"] = secondary(pairs)
         line["secondary"].append(reduce_secondary())
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        if any(kind.endswith(sfx) for sfx in TRANS_SUFFIXES):
+            host = synth.operands(w)   # the oracle leg reads the as-given layout
         line["cpu_baseline"] = cpu_baseline(w, host, args.cpu_budget)
     else:
         line["cpu_baseline"] = None

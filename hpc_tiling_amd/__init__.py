@@ -21,9 +21,10 @@ __all__ = [
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
-    "mi_reduce_sum_max_additions",
+    "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex",
     "sgemm", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace", "reduce_sum",
     "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "KERNEL_SPLITK_ATOMIC", "EXPORTED_SYMBOLS",
+    "OP_N", "OP_T",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libmi_sgemm.so"
@@ -41,12 +42,15 @@ KERNEL_VALU = 1
 KERNEL_SPLITK = 2
 KERNEL_SPLITK_ATOMIC = 3
 
+OP_N = 0  # operand as given
+OP_T = 1  # operand given transposed (A stored k x m, B stored n x k)
+
 EXPORTED_SYMBOLS = (
     "mi_sgemm", "mi_sgemm_valu", "mi_sgemm_splitk_workspace_bytes", "mi_sgemm_splitk",
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
-    "mi_reduce_sum_max_additions",
+    "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex",
 )
 
 if not LIB_PATH.exists():
@@ -91,13 +95,17 @@ lib.mi_sgemm.argtypes = _GEMM_ARGS + [_vp]
 lib.mi_sgemm.restype = _i
 lib.mi_sgemm_valu.argtypes = _GEMM_ARGS + [_vp]
 lib.mi_sgemm_valu.restype = _i
-lib.mi_sgemm_with_config.argtypes = [_i, _i] + _GEMM_ARGS + [_vp]
+lib.mi_sgemm_ex.argtypes = [_i, _i] + _GEMM_ARGS + [_vp]
+lib.mi_sgemm_ex.restype = _i
+lib.mi_sgemm_with_config.argtypes = [_i, _i, _i, _i] + _GEMM_ARGS + [_vp]
 lib.mi_sgemm_with_config.restype = _i
 lib.mi_sgemm_splitk_workspace_bytes.argtypes = [_i, _i, _i, _i]
 lib.mi_sgemm_splitk_workspace_bytes.restype = _sz
 lib.mi_sgemm_splitk.argtypes = _GEMM_ARGS + [_i, _vp, _sz, _vp]
 lib.mi_sgemm_splitk.restype = _i
-lib.mi_sgemm_splitk_with_config.argtypes = [_i] + _GEMM_ARGS + [_i, _vp, _sz, _vp]
+lib.mi_sgemm_splitk_ex.argtypes = [_i, _i] + _GEMM_ARGS + [_i, _vp, _sz, _vp]
+lib.mi_sgemm_splitk_ex.restype = _i
+lib.mi_sgemm_splitk_with_config.argtypes = [_i, _i, _i] + _GEMM_ARGS + [_i, _vp, _sz, _vp]
 lib.mi_sgemm_splitk_with_config.restype = _i
 lib.mi_sgemm_splitk_with_config_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.mi_sgemm_splitk_with_config_workspace_bytes.restype = _sz
@@ -134,10 +142,16 @@ def mi_sgemm_valu(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> 
     return lib.mi_sgemm_valu(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
-def mi_sgemm_with_config(kernel, config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
-                         stream=None) -> int:
-    return lib.mi_sgemm_with_config(kernel, config, m, n, k, alpha, A, lda, B, ldb, beta, C,
-                                    ldc, stream)
+def mi_sgemm_ex(trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                stream=None) -> int:
+    return lib.mi_sgemm_ex(trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                           stream)
+
+
+def mi_sgemm_with_config(kernel, config, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb,
+                         beta, C, ldc, stream=None) -> int:
+    return lib.mi_sgemm_with_config(kernel, config, trans_a, trans_b, m, n, k, alpha, A, lda,
+                                    B, ldb, beta, C, ldc, stream)
 
 
 def mi_sgemm_splitk_workspace_bytes(m, n, k, splits=0) -> int:
@@ -150,10 +164,16 @@ def mi_sgemm_splitk(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws, ws
                                ws_bytes, stream)
 
 
-def mi_sgemm_splitk_with_config(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits,
-                                ws, ws_bytes, stream=None) -> int:
-    return lib.mi_sgemm_splitk_with_config(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
-                                           splits, ws, ws_bytes, stream)
+def mi_sgemm_splitk_ex(trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                       ws, ws_bytes, stream=None) -> int:
+    return lib.mi_sgemm_splitk_ex(trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C,
+                                  ldc, splits, ws, ws_bytes, stream)
+
+
+def mi_sgemm_splitk_with_config(config, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta,
+                                C, ldc, splits, ws, ws_bytes, stream=None) -> int:
+    return lib.mi_sgemm_splitk_with_config(config, trans_a, trans_b, m, n, k, alpha, A, lda, B,
+                                           ldb, beta, C, ldc, splits, ws, ws_bytes, stream)
 
 
 def mi_sgemm_splitk_with_config_workspace_bytes(config, m, n, k, splits=0) -> int:
@@ -197,7 +217,7 @@ def mi_sgemm_config_count(kernel) -> int:
 # ---------------------------------------------------------------------------
 # torch tensor helpers
 # ---------------------------------------------------------------------------
-def _operand(t, name):
+def _check_tensor(t, name):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -207,10 +227,29 @@ def _operand(t, name):
         raise ValueError(f"{name} must be a device tensor")
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
-    if t.shape[1] > 1 and t.stride(1) != 1:
+
+
+def _layout(t, name):
+    """(pointer, ld, transposed) of a 2-D float32 device tensor: row-major
+    (unit column stride; ld = row stride) or column-major (unit row stride,
+    i.e. the transpose of a row-major matrix; ld = column stride)."""
+    _check_tensor(t, name)
+    r, c = t.shape
+    if c <= 1 or t.stride(1) == 1:
+        ld = max(t.stride(0), c, 1) if r > 1 else max(c, 1)
+        return t.data_ptr(), ld, OP_N
+    if r <= 1 or t.stride(0) == 1:
+        ld = max(t.stride(1), r, 1) if c > 1 else max(r, 1)
+        return t.data_ptr(), ld, OP_T
+    raise ValueError(f"{name} must be row-major or column-major (one unit stride)")
+
+
+def _operand(t, name):
+    """(pointer, ld) of a row-major operand."""
+    p, ld, trans = _layout(t, name)
+    if trans != OP_N:
         raise ValueError(f"{name} must be row-major (unit column stride)")
-    ld = max(t.stride(0), t.shape[1], 1) if t.shape[0] > 1 else max(t.shape[1], 1)
-    return t.data_ptr(), ld
+    return p, ld
 
 
 def _stream(stream):
@@ -220,7 +259,7 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _prepare(A, B, C, beta):
+def _output(A, B, C, beta):
     import torch
     m, k = A.shape
     k2, n = B.shape
@@ -232,30 +271,51 @@ def _prepare(A, B, C, beta):
         C = torch.empty((m, n), dtype=torch.float32, device=A.device)
     if tuple(C.shape) != (m, n):
         raise ValueError(f"C is {tuple(C.shape)}, expected {(m, n)}")
+    return m, n, k, C
+
+
+def _prepare(A, B, C, beta):
+    """Row-major A, B and C (the VALU and atomic paths)."""
+    m, n, k, C = _output(A, B, C, beta)
     pa, lda = _operand(A, "A")
     pb, ldb = _operand(B, "B")
     pc, ldc = _operand(C, "C")
     return m, n, k, pa, lda, pb, ldb, C, pc, ldc
 
 
+def _prepare_ex(A, B, C, beta):
+    """Operands in either storage order.  A column-major C is written as its
+    row-major transpose: C^T = op(B)^T op(A)^T, i.e. the call with A and B
+    swapped, each with its transpose flag flipped."""
+    m, n, k, C = _output(A, B, C, beta)
+    pa, lda, ta = _layout(A, "A")
+    pb, ldb, tb = _layout(B, "B")
+    pc, ldc, tc = _layout(C, "C")
+    if tc == OP_N:
+        return (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc
+    return (1 - tb, 1 - ta, n, m, k, pb, ldb, pa, lda), C, pc, ldc
+
+
 def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
     """C <- alpha * A @ B + beta * C on the matrix cores; returns C.
-    A (m x k), B (k x n), C (m x n): float32 device tensors, row-major
-    (row strides are passed as leading dimensions)."""
-    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
+    A (m x k), B (k x n), C (m x n): float32 device tensors, each row-major
+    or column-major (a transposed view such as ``X.t()`` is passed as the
+    transposed operand, without a copy)."""
+    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc = _prepare_ex(A, B, C, beta)
     s = _stream(stream)
     if config is None:
-        st = lib.mi_sgemm(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, s)
+        st = lib.mi_sgemm_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, s)
     else:
-        st = lib.mi_sgemm_with_config(KERNEL_MFMA, config, m, n, k, alpha, pa, lda, pb, ldb,
-                                      beta, pc, ldc, s)
+        st = lib.mi_sgemm_with_config(KERNEL_MFMA, config, ta, tb, m, n, k, alpha, pa, lda, pb,
+                                      ldb, beta, pc, ldc, s)
     if st != SUCCESS:
-        raise MiSgemmError(st, "mi_sgemm")
+        raise MiSgemmError(st, "mi_sgemm_ex")
     return C
 
 
 def sgemm_valu(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
-    """Same as sgemm, on the register-tiled VALU kernel."""
+    """Same as sgemm (row-major operands only), on the register-tiled VALU
+    kernel."""
     m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
     st = lib.mi_sgemm_valu(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, _stream(stream))
     if st != SUCCESS:
@@ -279,25 +339,25 @@ def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, st
     """Same as sgemm with the k range split into slices; `workspace` is a
     device tensor of at least mi_sgemm_splitk_workspace_bytes bytes (allocated
     here when None).  `config` forces the partial kernel's tile configuration."""
-    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
+    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc = _prepare_ex(A, B, C, beta)
     if workspace is None:
         workspace = splitk_workspace(m, n, k, splits, device=A.device, config=config)
     ws_bytes = workspace.numel() * workspace.element_size()
     if config is None:
-        st = lib.mi_sgemm_splitk(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
-                                 workspace.data_ptr(), ws_bytes, _stream(stream))
+        st = lib.mi_sgemm_splitk_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
+                                    splits, workspace.data_ptr(), ws_bytes, _stream(stream))
     else:
-        st = lib.mi_sgemm_splitk_with_config(config, m, n, k, alpha, pa, lda, pb, ldb, beta, pc,
-                                             ldc, splits, workspace.data_ptr(), ws_bytes,
-                                             _stream(stream))
+        st = lib.mi_sgemm_splitk_with_config(config, ta, tb, m, n, k, alpha, pa, lda, pb, ldb,
+                                             beta, pc, ldc, splits, workspace.data_ptr(),
+                                             ws_bytes, _stream(stream))
     if st != SUCCESS:
-        raise MiSgemmError(st, "mi_sgemm_splitk")
+        raise MiSgemmError(st, "mi_sgemm_splitk_ex")
     return C
 
 
 def sgemm_splitk_atomic(A, B, C=None, alpha=1.0, beta=0.0, splits=0, stream=None):
-    """Split-K with atomic accumulation into C (no workspace; not bitwise
-    reproducible run to run)."""
+    """Split-K with atomic accumulation into C (row-major operands; no
+    workspace; not bitwise reproducible run to run)."""
     m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
     st = lib.mi_sgemm_splitk_atomic(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
                                     _stream(stream))

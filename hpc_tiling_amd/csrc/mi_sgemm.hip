@@ -22,19 +22,35 @@ using KernelFn = void (*)(GemmArgs);
 // ---------------------------------------------------------------------------
 // Tile configurations of the matrix-core kernel.
 // ---------------------------------------------------------------------------
+// Kernel tables are indexed [trans_a][trans_b][vector loads].
 struct MfmaConfig {
     int bm, bn, bk, wgm, wgn;
-    KernelFn vec, scalar;                // full-k kernels
-    KernelFn split_vec, split_scalar;    // split-K partial kernels
-    KernelFn atomic_vec, atomic_scalar;  // split-K kernels adding into C atomically
+    KernelFn full[2][2][2];   // full-k kernels
+    KernelFn split[2][2][2];  // split-K partial kernels
+    KernelFn atomic[2];       // split-K kernels adding into C atomically (operands as given)
 };
+
+template <class T, int MODE, bool TA, bool TB>
+constexpr void fill_pair(KernelFn (&f)[2]) {
+    f[0] = &sgemm_mfma_kernel<T, false, MODE, TA, TB>;
+    f[1] = &sgemm_mfma_kernel<T, true, MODE, TA, TB>;
+}
+
+template <class T, int MODE>
+constexpr void fill_table(KernelFn (&f)[2][2][2]) {
+    fill_pair<T, MODE, false, false>(f[0][0]);
+    fill_pair<T, MODE, false, true>(f[0][1]);
+    fill_pair<T, MODE, true, false>(f[1][0]);
+    fill_pair<T, MODE, true, true>(f[1][1]);
+}
 
 template <class T>
 constexpr MfmaConfig make_cfg() {
-    return MfmaConfig{T::BM, T::BN, T::BK, T::WGM, T::WGN,
-                      &sgemm_mfma_kernel<T, true, kFull>, &sgemm_mfma_kernel<T, false, kFull>,
-                      &sgemm_mfma_kernel<T, true, kPartial>, &sgemm_mfma_kernel<T, false, kPartial>,
-                      &sgemm_mfma_kernel<T, true, kAtomic>, &sgemm_mfma_kernel<T, false, kAtomic>};
+    MfmaConfig c{T::BM, T::BN, T::BK, T::WGM, T::WGN, {}, {}, {}};
+    fill_table<T, kFull>(c.full);
+    fill_table<T, kPartial>(c.split);
+    fill_pair<T, kAtomic, false, false>(c.atomic);
+    return c;
 }
 
 // MfmaTile<BM, BN, BK, waves along m, waves along n>
@@ -148,9 +164,13 @@ SplitPlan plan_split(int m, int n, int k, int splits, int config) {
 // ---------------------------------------------------------------------------
 // Checks shared by every entry point.
 // ---------------------------------------------------------------------------
-int check_sizes(int m, int n, int k, int lda, int ldb, int ldc) {
+// Transpose flags are 0 (operand as given) or 1 (given transposed).  A
+// stored row width is k for A and n for B, or m and k when transposed.
+int check_sizes(int m, int n, int k, int lda, int ldb, int ldc, int ta = 0, int tb = 0) {
     if (m < 0 || n < 0 || k < 0) return MI_SGEMM_ERROR_INVALID_VALUE;
-    if (lda < (k > 1 ? k : 1) || ldb < (n > 1 ? n : 1) || ldc < (n > 1 ? n : 1))
+    if ((ta != 0 && ta != 1) || (tb != 0 && tb != 1)) return MI_SGEMM_ERROR_INVALID_VALUE;
+    const int wa = ta ? m : k, wb = tb ? k : n;
+    if (lda < (wa > 1 ? wa : 1) || ldb < (wb > 1 ? wb : 1) || ldc < (n > 1 ? n : 1))
         return MI_SGEMM_ERROR_INVALID_LD;
     return MI_SGEMM_SUCCESS;
 }
@@ -222,9 +242,10 @@ GemmArgs base_args(int m, int n, int k, float alpha, const float *A, int lda, co
 // Common prologue of the compute entry points.  Returns SUCCESS with
 // *done = true when the call is complete without a GEMM kernel.
 int prologue(int m, int n, int k, float alpha, const float *A, int lda, const float *B, int ldb,
-             float beta, float *C, int ldc, hipStream_t stream, bool *done) {
+             float beta, float *C, int ldc, hipStream_t stream, bool *done, int ta = 0,
+             int tb = 0) {
     *done = true;
-    int st = check_sizes(m, n, k, lda, ldb, ldc);
+    int st = check_sizes(m, n, k, lda, ldb, ldc, ta, tb);
     if (st) return st;
     st = check_pointers(m, n, k, alpha, A, B, C);
     if (st) return st;
@@ -236,12 +257,12 @@ int prologue(int m, int n, int k, float alpha, const float *A, int lda, const fl
     return MI_SGEMM_SUCCESS;
 }
 
-int run_mfma(int config, int m, int n, int k, float alpha, const float *A, int lda,
-             const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+int run_mfma(int config, int ta, int tb, int m, int n, int k, float alpha, const float *A,
+             int lda, const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
     if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     bool done;
-    int st = prologue(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, &done);
+    int st = prologue(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, &done, ta, tb);
     if (st || done) return st;
     const int id = config < 0 ? choose_mfma_config(m, n, k) : config;
     const MfmaConfig &c = kMfmaConfigs[id];
@@ -249,7 +270,7 @@ int run_mfma(int config, int m, int n, int k, float alpha, const float *A, int l
     a.tiles_m = (int)ceil_div(m, c.bm);
     a.tiles_n = (int)ceil_div(n, c.bn);
     const long long grid = (long long)a.tiles_m * a.tiles_n;
-    return launch(vector_ok(A, lda, B, ldb) ? c.vec : c.scalar, grid, 64 * c.wgm * c.wgn, s, a);
+    return launch(c.full[ta][tb][vector_ok(A, lda, B, ldb)], grid, 64 * c.wgm * c.wgn, s, a);
 }
 
 int run_valu(int config, int m, int n, int k, float alpha, const float *A, int lda,
@@ -267,11 +288,11 @@ int run_valu(int config, int m, int n, int k, float alpha, const float *A, int l
     return launch(fn, grid, ValuTile::NT, s, a);
 }
 
-int run_splitk(int config, int m, int n, int k, float alpha, const float *A, int lda,
-               const float *B, int ldb, float beta, float *C, int ldc, int splits, void *ws,
-               size_t ws_bytes, void *stream) {
+int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, const float *A,
+               int lda, const float *B, int ldb, float beta, float *C, int ldc, int splits,
+               void *ws, size_t ws_bytes, void *stream) {
     if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
-    int st = check_sizes(m, n, k, lda, ldb, ldc);
+    int st = check_sizes(m, n, k, lda, ldb, ldc, ta, tb);
     if (st) return st;
     if (splits < 0 || splits > k) return MI_SGEMM_ERROR_INVALID_VALUE;
     st = check_pointers(m, n, k, alpha, A, B, C);
@@ -298,8 +319,7 @@ int run_splitk(int config, int m, int n, int k, float alpha, const float *A, int
     a.ws = wsa;
     a.ws_slice = sp.slice;
     const long long grid = (long long)a.tiles_m * a.tiles_n * sp.splits;
-    st = launch(vector_ok(A, lda, B, ldb) ? c.split_vec : c.split_scalar, grid,
-                64 * c.wgm * c.wgn, s, a);
+    st = launch(c.split[ta][tb][vector_ok(A, lda, B, ldb)], grid, 64 * c.wgm * c.wgn, s, a);
     if (st) return st;
 
     const long long blocks = ceil_div(ceil_div((long long)m * n, 64), 4);
@@ -363,7 +383,12 @@ extern "C" {
 
 int mi_sgemm(int m, int n, int k, float alpha, const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, void *stream) {
-    return run_mfma(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run_mfma(-1, 0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int mi_sgemm_ex(int trans_a, int trans_b, int m, int n, int k, float alpha, const float *A,
+                int lda, const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+    return run_mfma(-1, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int mi_sgemm_valu(int m, int n, int k, float alpha, const float *A, int lda, const float *B,
@@ -371,12 +396,13 @@ int mi_sgemm_valu(int m, int n, int k, float alpha, const float *A, int lda, con
     return run_valu(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
-int mi_sgemm_with_config(int kernel, int config, int m, int n, int k, float alpha,
-                         const float *A, int lda, const float *B, int ldb, float beta, float *C,
-                         int ldc, void *stream) {
+int mi_sgemm_with_config(int kernel, int config, int trans_a, int trans_b, int m, int n, int k,
+                         float alpha, const float *A, int lda, const float *B, int ldb,
+                         float beta, float *C, int ldc, void *stream) {
     if (kernel == MI_SGEMM_KERNEL_MFMA)
-        return run_mfma(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
-    if (kernel == MI_SGEMM_KERNEL_VALU)
+        return run_mfma(config, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                        stream);
+    if (kernel == MI_SGEMM_KERNEL_VALU && trans_a == 0 && trans_b == 0)
         return run_valu(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     return MI_SGEMM_ERROR_INVALID_VALUE;
 }
@@ -388,15 +414,23 @@ size_t mi_sgemm_splitk_workspace_bytes(int m, int n, int k, int splits) {
 int mi_sgemm_splitk(int m, int n, int k, float alpha, const float *A, int lda, const float *B,
                     int ldb, float beta, float *C, int ldc, int splits, void *ws,
                     size_t ws_bytes, void *stream) {
-    return run_splitk(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws, ws_bytes,
-                      stream);
+    return run_splitk(-1, 0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws,
+                      ws_bytes, stream);
 }
 
-int mi_sgemm_splitk_with_config(int config, int m, int n, int k, float alpha, const float *A,
-                                int lda, const float *B, int ldb, float beta, float *C, int ldc,
-                                int splits, void *ws, size_t ws_bytes, void *stream) {
-    return run_splitk(config, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, ws, ws_bytes,
-                      stream);
+int mi_sgemm_splitk_ex(int trans_a, int trans_b, int m, int n, int k, float alpha,
+                       const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                       int ldc, int splits, void *ws, size_t ws_bytes, void *stream) {
+    return run_splitk(-1, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                      ws, ws_bytes, stream);
+}
+
+int mi_sgemm_splitk_with_config(int config, int trans_a, int trans_b, int m, int n, int k,
+                                float alpha, const float *A, int lda, const float *B, int ldb,
+                                float beta, float *C, int ldc, int splits, void *ws,
+                                size_t ws_bytes, void *stream) {
+    return run_splitk(config, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                      splits, ws, ws_bytes, stream);
 }
 
 int mi_sgemm_splitk_atomic(int m, int n, int k, float alpha, const float *A, int lda,

@@ -22,16 +22,28 @@
 // k = 8g+s and 8g+4+s, so the four MFMAs cover the eight k values of the
 // group exactly once with matching A and B indices.
 //
+// Operand layouts.  Each operand supplies an E x BK slice per k step (E = BM
+// for A, BN for B) and sits in memory in one of two layouts:
+//   * k-contiguous: element (e, t) at X[e*ld + t] -- A as given, or B given
+//     transposed (B^T stored n x k);
+//   * e-contiguous: element (e, t) at X[t*ld + e] -- B as given, or A given
+//     transposed (A^T stored k x m).
+// The LDS tile keeps the memory layout (a direct load cannot transpose), and
+// the fragment read adapts to it: from a k-contiguous tile one 16-byte read
+// gives the four k values above; from an e-contiguous tile four 4-byte reads
+// (one per k row) do.  Transposed reads are the bank-conflict case of page
+// "GEMM优化原理" (section 基于 register 计算); the swizzles below remove them.
+//
 // LDS layout (64 banks of 4 bytes; a direct load writes 64 lanes x 16 bytes
 // to 1 KiB of consecutive LDS, so tiles are unpadded and XOR-swizzled in
 // 16-byte chunks instead):
-//   * A: BM rows of BK floats (m-major, as in memory); logical chunk c of row
-//     r sits at chunk c ^ swz(r), swz(r) = (r * CA / 16) % CA with CA = BK / 4
+//   * k-contiguous tile: E rows of BK floats; logical chunk c of row r sits
+//     at chunk c ^ swz(r), swz(r) = (r * CH / 16) % CH with CH = BK / 4
 //     chunks per row.  The 16 lanes of a fragment read (16 consecutive rows,
 //     same logical chunk) then cover all 16 bank quads.
-//   * B: BK rows of BN floats (k-major, as in memory); rows with bit 2 set
-//     swap the two 32-float halves of every 64 floats.  The lane halves of a
-//     fragment read take rows k and k+4, which then fall on disjoint banks.
+//   * e-contiguous tile: BK rows of E floats; rows with bit 2 set swap the two
+//     32-float halves of every 64 floats.  The lane halves of a fragment read
+//     take rows k and k+4, which then fall on disjoint banks.
 #pragma once
 
 #include <type_traits>
@@ -49,20 +61,99 @@ struct MfmaTile {
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // per-wave tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 blocks per wave
     static constexpr int GROUPS = BK / 8;                 // groups of 8 k per step
-    static constexpr int CA = BK / 4;                     // 16-byte chunks per A row
-    static constexpr int CB = BN / 4;                     // 16-byte chunks per B row
-    static constexpr int A_PER = BM * CA / NT;            // A chunks per thread per step
-    static constexpr int B_PER = BK * CB / NT;            // B chunks per thread per step
     static constexpr int LDS_BYTES = STAGES * (BM * BK + BK * BN) * 4;
-    static_assert(BK == 16 || BK == 32, "A swizzle assumes 4 or 8 chunks per row");
-    static_assert(BN % 64 == 0, "B swizzle swaps 32-float halves of 64-float blocks");
     static_assert(GROUPS % 2 == 0, "fragment double-buffering needs an even group count");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BM * CA % NT == 0 && BK * CB % NT == 0, "load slots must divide evenly");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
+};
 
-    __device__ static constexpr int a_swz(int row) { return (row * CA / 16) % CA; }
-    __device__ static constexpr int b_swz(int krow) { return 8 * ((krow >> 2) & 1); }
+// Four floats of an e-contiguous fragment (read one by one).
+struct Vals4 {
+    float v[4];
+    __device__ float &operator[](int s) { return v[s]; }
+    __device__ float operator[](int s) const { return v[s]; }
+};
+
+// Staging and fragment reads of one operand (E = BM or BN) of tile T.
+// KROWS: the operand is e-contiguous, so LDS rows are k rows.
+template <class T, int E, bool KROWS>
+struct Operand {
+    static constexpr int ROWS = KROWS ? T::BK : E;         // LDS tile rows
+    static constexpr int CH = KROWS ? E / 4 : T::BK / 4;   // 16-byte chunks per row
+    static constexpr int PER = ROWS * CH / T::NT;          // chunks per thread per step
+    static constexpr int ELEMS = E * T::BK;
+    using Frag = std::conditional_t<KROWS, Vals4, f32x4>;  // four k values of one lane
+    static_assert(KROWS ? E % 64 == 0 : (T::BK == 16 || T::BK == 32),
+                  "swizzle assumes 64-float rows (e-contiguous) or 4 or 8 chunks per row");
+    static_assert(ROWS * CH % T::NT == 0, "load slots must divide evenly");
+
+    __device__ static constexpr int swz(int row) {
+        return KROWS ? 8 * ((row >> 2) & 1) : (row * CH / 16) % CH;
+    }
+    // Chunk q = tid + i * NT of a tile (the chunk lane `lane` of wave `wave`
+    // writes in the i-th load instruction): its LDS row and logical chunk.
+    __device__ static void chunk(int tid, int i, int &row, int &c) {
+        const int q = tid + i * T::NT;
+        row = q / CH;
+        c = (q % CH) ^ swz(row);
+    }
+    // Largest in-range coordinate on the e edge, in the unit the clamp of a
+    // direct load uses: a row (k-contiguous) or a chunk (e-contiguous).
+    __device__ static int clamp_limit(int e_valid) { return KROWS ? (e_valid - 1) >> 2 : e_valid - 1; }
+    // First element of the workgroup's e range (e0 = its first row of op(X)),
+    // and from there the first element of the tile of k step k0.
+    __device__ static const float *block_base(const float *X, long long ld, int e0) {
+        return KROWS ? X + e0 : X + (long long)e0 * ld;
+    }
+    __device__ static const float *tile_base(const float *blk, long long ld, int k0) {
+        return KROWS ? blk + (long long)k0 * ld : blk + k0;
+    }
+    // Byte offset from the tile base of chunk (row, c), edge rows or chunks
+    // clamped to `lim` (they feed only outputs that are never stored).
+    __device__ static int direct_offset(int row, int c, long long ld, int lim) {
+        return KROWS ? (int)(4 * ((long long)row * ld + 4 * min(c, lim)))
+                     : (int)(4 * ((long long)min(row, lim) * ld + 4 * c));
+    }
+    // Direct loads need every byte offset of a tile to fit the 31-bit range.
+    __device__ static bool direct_fits(long long ld) {
+        return ld < (1LL << 31) / (4LL * (KROWS ? T::BK : E));
+    }
+    // Masked 16-byte load of chunk (row, c) of the tile at (e0, k0): elements
+    // with e >= e_end or k >= k_end read as zero.
+    template <bool VEC>
+    __device__ static f32x4 load_masked(const float *X, long long ld, int e0, int e_end, int k0,
+                                        int k_end, int row, int c) {
+        if (KROWS) {
+            const float *src = X + (long long)(k0 + row) * ld + e0 + 4 * c;
+            const int valid = (k0 + row < k_end) ? min(4, e_end - (e0 + 4 * c)) : 0;
+            return load4_masked<VEC>(src, valid);
+        } else {
+            const float *src = X + (long long)(e0 + row) * ld + k0 + 4 * c;
+            const int valid = (e0 + row < e_end) ? min(4, k_end - (k0 + 4 * c)) : 0;
+            return load4_masked<VEC>(src, valid);
+        }
+    }
+    // Per-lane fragment addressing for the 32-row block starting at wave-tile
+    // coordinate e_blk: lane (l, h) = (lane % 32, lane / 32).
+    __device__ static void frag_setup(int e_blk, int li, int lh, int &off, int &sw) {
+        const int e = e_blk + li;
+        if (KROWS) {
+            off = (e ^ (32 * lh)) + 4 * lh * E;
+            sw = 0;
+        } else {
+            off = e * T::BK;
+            sw = swz(e);
+        }
+    }
+    // The four values lane (l, h) feeds MFMAs s = 0..3 of group g: X[e][8g+4h+s].
+    __device__ static void frag_read(Frag &f, const float *buf, int off, int sw, int g, int lh) {
+        if constexpr (KROWS) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) f[s] = buf[off + (8 * g + s) * E];
+        } else {
+            f = *reinterpret_cast<const f32x4 *>(buf + off + 4 * ((2 * g + lh) ^ sw));
+        }
+    }
 };
 
 // Word 3 of a raw (untyped) buffer resource on gfx9-class parts: 32-bit data
@@ -101,18 +192,20 @@ __device__ __forceinline__ void load_lds16(const float *base, float *lds, int vo
 // same barrier (which waits for the direct loads), so the first fragments of
 // step t+1 can be read before the barrier of step t and the MFMA stream does
 // not wait for LDS at a step boundary.
-template <class T, bool VEC, int MODE>
+template <class T, bool VEC, int MODE, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     constexpr bool SPLIT = MODE != kFull;
+    using OA = Operand<T, T::BM, TA>;    // A: k-contiguous unless given transposed
+    using OB = Operand<T, T::BN, !TB>;   // B: n-contiguous unless given transposed
     // One LDS object per ring stage, always indexed at compile time: the
     // compiler can then tell the buffer a direct load writes from the buffers
     // being read, and does not hold the MFMAs back until the load lands.
-    __shared__ __attribute__((aligned(1024))) float As0[T::BM * T::BK];
-    __shared__ __attribute__((aligned(1024))) float As1[T::BM * T::BK];
-    __shared__ __attribute__((aligned(1024))) float As2[T::BM * T::BK];
-    __shared__ __attribute__((aligned(1024))) float Bs0[T::BK * T::BN];
-    __shared__ __attribute__((aligned(1024))) float Bs1[T::BK * T::BN];
-    __shared__ __attribute__((aligned(1024))) float Bs2[T::BK * T::BN];
+    __shared__ __attribute__((aligned(1024))) float As0[OA::ELEMS];
+    __shared__ __attribute__((aligned(1024))) float As1[OA::ELEMS];
+    __shared__ __attribute__((aligned(1024))) float As2[OA::ELEMS];
+    __shared__ __attribute__((aligned(1024))) float Bs0[OB::ELEMS];
+    __shared__ __attribute__((aligned(1024))) float Bs1[OB::ELEMS];
+    __shared__ __attribute__((aligned(1024))) float Bs2[OB::ELEMS];
     auto a_buf = [&](auto s) -> float * {
         constexpr int S = decltype(s)::value;
         if constexpr (S == 0) return As0;
@@ -147,30 +240,15 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     const int nsteps = (kend - kbeg + T::BK - 1) / T::BK;
     // Whole k steps of aligned operands are loaded directly into LDS (byte
     // offsets inside one tile step must fit the 31-bit buffer offset).  On
-    // the m / n edge, rows of A past m and chunks of B past n are clamped to
-    // the last valid row / chunk: they only feed outputs that are never
-    // stored, and every address stays inside the operands.
-    const bool direct_ok = VEC && p.lda < (1LL << 31) / (4LL * T::BM) &&
-                           p.ldb < (1LL << 31) / (4LL * T::BK);
+    // the m / n edge, rows or chunks past the edge are clamped to the last
+    // valid one: they only feed outputs that are never stored, and every
+    // address stays inside the operands.
+    const bool direct_ok = VEC && OA::direct_fits(p.lda) && OB::direct_fits(p.ldb);
     const int ndirect = direct_ok ? (kend - kbeg) / T::BK : 0;
-    const int a_row_max = min(T::BM, p.m - m0) - 1;           // last valid row of the A tile
-    const int b_chunk_max = (min(T::BN, p.n - n0) - 1) >> 2;  // chunk holding column n-1
-
-    const float *Ablk = p.A + (long long)m0 * p.lda;
-    const float *Bblk = p.B + n0;
-
-    // Chunk q = tid + i * NT of a tile (the chunk lane `lane` of wave `wave`
-    // writes in the i-th load instruction): its row and logical chunk.
-    auto a_chunk = [&](int i, int &row, int &c) {
-        const int q = tid + i * T::NT;
-        row = q / T::CA;
-        c = (q % T::CA) ^ T::a_swz(row);
-    };
-    auto b_chunk = [&](int i, int &row, int &c) {
-        const int q = tid + i * T::NT;
-        row = q / T::CB;
-        c = (q % T::CB) ^ T::b_swz(row);
-    };
+    const int a_lim = OA::clamp_limit(min(T::BM, p.m - m0));
+    const int b_lim = OB::clamp_limit(min(T::BN, p.n - n0));
+    const float *Ablk = OA::block_base(p.A, p.lda, m0);
+    const float *Bblk = OB::block_base(p.B, p.ldb, n0);
 
     // ---- direct global -> LDS loads (complete, aligned tiles) ---------------
     // buffer_load_dwordx4 ... lds through a per-step buffer resource whose
@@ -181,54 +259,48 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     auto load_direct = [&](int step, auto buf) {
         float *as = a_buf(buf), *bs = b_buf(buf);
         const int k0 = kbeg + step * T::BK;
-        const float *abase = Ablk + k0;
-        const float *bbase = Bblk + (long long)k0 * p.ldb;
+        const float *abase = OA::tile_base(Ablk, p.lda, k0);
+        const float *bbase = OB::tile_base(Bblk, p.ldb, k0);
 #pragma unroll
-        for (int i = 0; i < T::A_PER; ++i) {
+        for (int i = 0; i < OA::PER; ++i) {
             int row, c;
-            a_chunk(i, row, c);
-            load_lds16(abase, as + (i * T::WAVES + wave) * 256,
-                       (int)(4 * ((long long)min(row, a_row_max) * p.lda + 4 * c)));
+            OA::chunk(tid, i, row, c);
+            load_lds16(abase, as + (i * T::WAVES + wave) * 256, OA::direct_offset(row, c, p.lda, a_lim));
         }
 #pragma unroll
-        for (int i = 0; i < T::B_PER; ++i) {
+        for (int i = 0; i < OB::PER; ++i) {
             int row, c;
-            b_chunk(i, row, c);
-            load_lds16(bbase, bs + (i * T::WAVES + wave) * 256,
-                       (int)(4 * ((long long)row * p.ldb + 4 * min(c, b_chunk_max))));
+            OB::chunk(tid, i, row, c);
+            load_lds16(bbase, bs + (i * T::WAVES + wave) * 256, OB::direct_offset(row, c, p.ldb, b_lim));
         }
     };
 
     // ---- masked loads through VGPRs (edges, k tail, unaligned) -------------
     struct Stage {
-        f32x4 a[T::A_PER], b[T::B_PER];
+        f32x4 a[OA::PER], b[OB::PER];
     };
     auto load_regs = [&](Stage &st, int step) {
         const int k0 = kbeg + step * T::BK;
 #pragma unroll
-        for (int i = 0; i < T::A_PER; ++i) {
+        for (int i = 0; i < OA::PER; ++i) {
             int row, c;
-            a_chunk(i, row, c);
-            const float *src = Ablk + (long long)row * p.lda + k0 + 4 * c;
-            const int valid = (m0 + row < p.m) ? min(4, kend - (k0 + 4 * c)) : 0;
-            st.a[i] = load4_masked<VEC>(src, valid);
+            OA::chunk(tid, i, row, c);
+            st.a[i] = OA::template load_masked<VEC>(p.A, p.lda, m0, p.m, k0, kend, row, c);
         }
 #pragma unroll
-        for (int i = 0; i < T::B_PER; ++i) {
+        for (int i = 0; i < OB::PER; ++i) {
             int row, c;
-            b_chunk(i, row, c);
-            const float *src = Bblk + (long long)(k0 + row) * p.ldb + 4 * c;
-            const int valid = (k0 + row < kend) ? min(4, p.n - (n0 + 4 * c)) : 0;
-            st.b[i] = load4_masked<VEC>(src, valid);
+            OB::chunk(tid, i, row, c);
+            st.b[i] = OB::template load_masked<VEC>(p.B, p.ldb, n0, p.n, k0, kend, row, c);
         }
     };
     auto store_regs = [&](const Stage &st, auto buf) {
         float *as = a_buf(buf), *bs = b_buf(buf);
 #pragma unroll
-        for (int i = 0; i < T::A_PER; ++i)
+        for (int i = 0; i < OA::PER; ++i)
             *reinterpret_cast<f32x4 *>(as + 4 * (tid + i * T::NT)) = st.a[i];
 #pragma unroll
-        for (int i = 0; i < T::B_PER; ++i)
+        for (int i = 0; i < OB::PER; ++i)
             *reinterpret_cast<f32x4 *>(bs + 4 * (tid + i * T::NT)) = st.b[i];
     };
 
@@ -242,31 +314,22 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
     const int li = lane & 31, lh = lane >> 5;
-    int a_row_off[T::FM], a_swz[T::FM], b_col[T::FN];
+    int a_off[T::FM], a_sw[T::FM], b_off[T::FN], b_sw[T::FN];
 #pragma unroll
-    for (int a = 0; a < T::FM; ++a) {
-        const int row = wm * T::WTM + 32 * a + li;
-        a_row_off[a] = row * T::BK;
-        a_swz[a] = T::a_swz(row);
-    }
+    for (int a = 0; a < T::FM; ++a) OA::frag_setup(wm * T::WTM + 32 * a, li, lh, a_off[a], a_sw[a]);
 #pragma unroll
-    for (int b = 0; b < T::FN; ++b)
-        b_col[b] = ((wn * T::WTN + 32 * b + li) ^ (32 * lh)) + 4 * lh * T::BN;
+    for (int b = 0; b < T::FN; ++b) OB::frag_setup(wn * T::WTN + 32 * b, li, lh, b_off[b], b_sw[b]);
 
     struct Frag {
-        f32x4 a[T::FM];
-        float b[T::FN][4];
+        typename OA::Frag a[T::FM];
+        typename OB::Frag b[T::FN];
     };
     auto read_frag = [&](Frag &f, auto buf, int g) {
         const float *as = a_buf(buf), *bs = b_buf(buf);
 #pragma unroll
-        for (int a = 0; a < T::FM; ++a)
-            f.a[a] = *reinterpret_cast<const f32x4 *>(
-                as + a_row_off[a] + 4 * ((2 * g + lh) ^ a_swz[a]));
+        for (int a = 0; a < T::FM; ++a) OA::frag_read(f.a[a], as, a_off[a], a_sw[a], g, lh);
 #pragma unroll
-        for (int b = 0; b < T::FN; ++b)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) f.b[b][s] = bs[b_col[b] + (8 * g + s) * T::BN];
+        for (int b = 0; b < T::FN; ++b) OB::frag_read(f.b[b], bs, b_off[b], b_sw[b], g, lh);
     };
     auto mfma_group = [&](const Frag &f) {
 #pragma unroll

@@ -13,7 +13,11 @@
  * in elements, between the starts of consecutive rows):
  *     A_it = A[i*lda + t],   B_tj = B[t*ldb + j],   C_ij = C[i*ldc + j].
  * Elements beyond the logical width of a row (the padding up to ld) are never
- * read or written.  Pointers need no particular alignment and ld values need
+ * read or written.  The _ex entry points also take A or B transposed (the
+ * BLAS op(X) = X^T): trans_a = 1 means A is stored k x m, A_it = A[t*lda + i]
+ * with lda >= max(1, m); trans_b = 1 means B is stored n x k,
+ * B_tj = B[j*ldb + t] with ldb >= max(1, k).  Column-major operands are the
+ * transposed row-major ones, so every BLAS storage order is covered.  Pointers need no particular alignment and ld values need
  * not be multiples of 4: 16-byte vector loads are used when A and B are
  * 16-byte aligned with lda and ldb multiples of 4, element loads otherwise.
  *
@@ -48,9 +52,11 @@ extern "C" {
 
 typedef enum mi_status {
     MI_SGEMM_SUCCESS = 0,
-    MI_SGEMM_ERROR_INVALID_VALUE = 1, /* m, n or k < 0; splits < 0 or > k;
-                                         unknown kernel or config id; grid too large */
-    MI_SGEMM_ERROR_INVALID_LD = 2,    /* lda < max(1,k), ldb < max(1,n) or ldc < max(1,n) */
+    MI_SGEMM_ERROR_INVALID_VALUE = 1, /* m, n or k < 0; splits < 0 or > k; a transpose
+                                         flag other than 0 or 1; unknown kernel or
+                                         config id; grid too large */
+    MI_SGEMM_ERROR_INVALID_LD = 2,    /* lda < max(1,k), ldb < max(1,n) or ldc < max(1,n)
+                                         (m for lda, k for ldb when transposed) */
     MI_SGEMM_ERROR_NULL_POINTER = 3,  /* NULL for an operand that would be read or written */
     MI_SGEMM_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than required */
     MI_SGEMM_ERROR_LAUNCH = 5,        /* the HIP runtime rejected a kernel launch */
@@ -73,6 +79,26 @@ typedef enum mi_status {
 int mi_sgemm(int m, int n, int k, float alpha,
              const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, void *stream);
+
+/* Transpose flags of the _ex entry points. */
+typedef enum mi_op {
+    MI_SGEMM_OP_N = 0, /* operand as given (A: m x k, B: k x n, row-major) */
+    MI_SGEMM_OP_T = 1  /* operand given transposed (A stored k x m, B stored n x k) */
+} mi_op;
+
+/*
+ * mi_sgemm_ex -- mi_sgemm with op(A) and op(B): C <- alpha * op(A) op(B) +
+ * beta * C.  A transposed operand is staged into LDS in its memory layout
+ * (m- or n-contiguous rows of k) and read back as MFMA fragments with a
+ * swizzle that keeps those transposed reads free of bank conflicts (the
+ * conflict case of page "GEMM优化原理", section 基于 register 计算).
+ * trans_a, trans_b: MI_SGEMM_OP_N or MI_SGEMM_OP_T.  Other arguments,
+ * semantics and errors as mi_sgemm; mi_sgemm(...) equals
+ * mi_sgemm_ex(MI_SGEMM_OP_N, MI_SGEMM_OP_N, ...).
+ */
+int mi_sgemm_ex(int trans_a, int trans_b, int m, int n, int k, float alpha,
+                const float *A, int lda, const float *B, int ldb,
+                float beta, float *C, int ldc, void *stream);
 
 /*
  * mi_sgemm_valu -- the register-tiled VALU path, kept as a measured
@@ -117,6 +143,16 @@ int mi_sgemm_splitk(int m, int n, int k, float alpha,
                     const float *A, int lda, const float *B, int ldb,
                     float beta, float *C, int ldc,
                     int splits, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * mi_sgemm_splitk_ex -- mi_sgemm_splitk with op(A) and op(B) as in
+ * mi_sgemm_ex.  The workspace size does not depend on the transposes
+ * (mi_sgemm_splitk_workspace_bytes).
+ */
+int mi_sgemm_splitk_ex(int trans_a, int trans_b, int m, int n, int k, float alpha,
+                       const float *A, int lda, const float *B, int ldb,
+                       float beta, float *C, int ldc,
+                       int splits, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * mi_sgemm_splitk_atomic -- split-K without a workspace, kept as a measured
@@ -217,25 +253,29 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
 int mi_sgemm_config_count(int kernel);
 
 /*
- * mi_sgemm_with_config -- mi_sgemm / mi_sgemm_valu with a forced tile
+ * mi_sgemm_with_config -- mi_sgemm_ex / mi_sgemm_valu with a forced tile
  * configuration (for measured comparisons of tilings and for tests that
  * cover every configuration).  kernel is MI_SGEMM_KERNEL_MFMA or
- * MI_SGEMM_KERNEL_VALU; config < 0 means the automatic choice.  Same
- * semantics and errors as mi_sgemm; an unknown config gives
+ * MI_SGEMM_KERNEL_VALU (the VALU path takes operands as given only:
+ * trans_a = trans_b = MI_SGEMM_OP_N); config < 0 means the automatic
+ * choice.  Same semantics and errors as mi_sgemm_ex; an unknown config gives
  * MI_SGEMM_ERROR_INVALID_VALUE.
  */
-int mi_sgemm_with_config(int kernel, int config, int m, int n, int k, float alpha,
+int mi_sgemm_with_config(int kernel, int config, int trans_a, int trans_b,
+                         int m, int n, int k, float alpha,
                          const float *A, int lda, const float *B, int ldb,
                          float beta, float *C, int ldc, void *stream);
 
 /*
  * mi_sgemm_splitk_with_config -- mi_sgemm_splitk with a forced tile
  * configuration of the partial kernel (ids as for MI_SGEMM_KERNEL_MFMA;
- * config < 0 means the automatic choice).  The workspace it needs is given
- * by mi_sgemm_splitk_with_config_workspace_bytes (0 for invalid arguments or
- * an unknown config).  Same semantics and errors as mi_sgemm_splitk.
+ * config < 0 means the automatic choice) and op(A), op(B) as in mi_sgemm_ex.
+ * The workspace it needs is given by
+ * mi_sgemm_splitk_with_config_workspace_bytes (0 for invalid arguments or an
+ * unknown config).  Same semantics and errors as mi_sgemm_splitk_ex.
  */
-int mi_sgemm_splitk_with_config(int config, int m, int n, int k, float alpha,
+int mi_sgemm_splitk_with_config(int config, int trans_a, int trans_b,
+                                int m, int n, int k, float alpha,
                                 const float *A, int lda, const float *B, int ldb,
                                 float beta, float *C, int ldc,
                                 int splits, void *ws, size_t ws_bytes, void *stream);

@@ -149,12 +149,44 @@ def test_splitk_atomic_argument_errors():
 def test_with_config_rejects_unknown_ids():
     n = hta.mi_sgemm_config_count(hta.KERNEL_MFMA)
     assert n >= 1
-    r = hta.mi_sgemm_with_config(hta.KERNEL_MFMA, n, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    r = hta.mi_sgemm_with_config(hta.KERNEL_MFMA, n, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
     assert r == hta.ERROR_INVALID_VALUE
-    r = hta.mi_sgemm_with_config(hta.KERNEL_VALU, 1, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    r = hta.mi_sgemm_with_config(hta.KERNEL_VALU, 1, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
     assert r == hta.ERROR_INVALID_VALUE
-    r = hta.mi_sgemm_with_config(5, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    r = hta.mi_sgemm_with_config(5, 0, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
     assert r == hta.ERROR_INVALID_VALUE
+    # the VALU kernel takes operands as given only
+    r = hta.mi_sgemm_with_config(hta.KERNEL_VALU, 0, 1, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    assert r == hta.ERROR_INVALID_VALUE
+    r = hta.mi_sgemm_splitk_with_config(n, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4, 0, P, 1 << 20)
+    assert r == hta.ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("entry", ["ex", "splitk_ex"])
+def test_transpose_argument_errors(entry):
+    """Leading dimensions are checked against the stored row width: k for A
+    and n for B as given, m for A^T and k for B^T; flags must be 0 or 1."""
+    E = hta
+    ws = 1 << 20
+
+    def f(ta, tb, m, n, k, lda, ldb, ldc, A=P, B=P, C=P):
+        if entry == "ex":
+            return hta.mi_sgemm_ex(ta, tb, m, n, k, 1.0, A, lda, B, ldb, 0.0, C, ldc)
+        return hta.mi_sgemm_splitk_ex(ta, tb, m, n, k, 1.0, A, lda, B, ldb, 0.0, C, ldc, 0, P, ws)
+
+    m, n, k = 6, 10, 8
+    # A^T is k x m: lda must be >= m (not k); B^T is n x k: ldb must be >= k (not n)
+    assert f(1, 0, m, n, k, m - 1, n, n) == E.ERROR_INVALID_LD
+    assert f(0, 1, m, n, k, k, k - 1, n) == E.ERROR_INVALID_LD
+    assert f(1, 1, m, n, k, m, k, n - 1) == E.ERROR_INVALID_LD
+    assert f(0, 0, m, n, k, k - 1, n, n) == E.ERROR_INVALID_LD
+    for bad in (-1, 2):
+        assert f(bad, 0, m, n, k, 16, 16, 16) == E.ERROR_INVALID_VALUE
+        assert f(0, bad, m, n, k, 16, 16, 16) == E.ERROR_INVALID_VALUE
+    assert f(1, 1, m, n, k, m, k, n, A=None) == E.ERROR_NULL_POINTER
+    # lda = m < k and ldb = k < n are valid for the transposed forms: the call
+    # gets past every argument check (no device here, or a no-op size)
+    assert f(1, 1, 0, n, k, 1, k, n) == E.SUCCESS
 
 
 def test_valid_call_without_gpu_reports_no_device():
