@@ -105,13 +105,29 @@ def setup(w, kind):
     return (A, B, C), (Ad, Bd, Cd), make_step(kind, w, Av, Bv, Cd[:, :w.n], ws)
 
 
-def time_steps(step, steps, warmup):
+SETTLE_S = 0.2
+LAST_EXTRA_WARMUP = [0]
+
+
+def time_steps(step, steps, warmup, settle_s=SETTLE_S):
     """Seconds for exactly `steps` calls after `warmup` untimed ones, measured
-    with events on the current stream (the stream the kernels are launched on)."""
+    with events on the current stream (the stream the kernels are launched on).
+    After an idle spell the GPU clock needs about 30 ms of load to reach its
+    steady value, so the untimed warmup continues (in batches of 10 calls,
+    counted in LAST_EXTRA_WARMUP) until at least `settle_s` seconds of
+    back-to-back calls have run."""
     import torch
+    start = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    extra = 0
+    while time.perf_counter() - start < settle_s:
+        for _ in range(10):
+            step()
+        extra += 10
+        torch.cuda.synchronize()
+    LAST_EXTRA_WARMUP[0] = extra
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -225,6 +241,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--reduce-only", action="store_true",
+                    help="only time the array sum on its largest workload (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -251,6 +269,10 @@ def main(argv=None):
                           "launches": 5}), flush=True)
         return 0
 
+    if args.reduce_only:
+        print(json.dumps({"reduce": reduce_secondary()}), flush=True)
+        return 0
+
     import synth
     from hpc_tiling_amd import perfmodel as pm
 
@@ -260,6 +282,7 @@ def main(argv=None):
     host, dev, step = setup(w, kind)
     print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
     dt = time_steps(step, args.steps, args.warmup)
+    extra_warmup = LAST_EXTRA_WARMUP[0]
     ms = 1e3 * dt / args.steps
     value = pm.tflops(w.m, w.n, w.k, dt, reps=args.steps)
 
@@ -286,6 +309,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_extra_steps": extra_warmup,   # untimed, until 0.2 s of load settles the clock
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",

@@ -369,6 +369,7 @@ int run_splitk_atomic(int config, int m, int n, int k, float alpha, const float 
 // gives each lane 128 inputs, the fastest point of a sweep over 8 to 64
 // workgroups per CU and unroll depths 4 to 16.
 long long reduce_grid(long long n) {
+    static_assert(32 * kCUs <= kFinalThreads * kFinalPer, "final pass covers every partial");
     long long g = ceil_div(n, (long long)kReduceThreads * 16);
     if (g > 32 * kCUs) g = 32 * kCUs;
     return g < 1 ? 1 : g;
@@ -457,8 +458,8 @@ long long mi_reduce_sum_max_additions(long long n) {
     const long long per_acc = ceil_div(ceil_div(n, 4), g * kReduceThreads);  // float4s per lane
     // per accumulator (+1 for a trailing element), 2 levels over the four
     // accumulators, 6 in the wave, 2 over the waves; then the final pass:
-    // ceil(g / 256) in a lane, 6 + 2 levels.
-    return per_acc + 1 + 2 + 6 + 2 + ceil_div(g, kReduceThreads) + 6 + 2;
+    // kFinalPer - 1 in a lane, 6 in the wave, 6 over the per-wave sums.
+    return per_acc + 1 + 2 + 6 + 2 + (kFinalPer - 1) + 6 + 6;
 }
 
 int mi_reduce_sum(long long n, const float *x, float *out, void *ws, size_t ws_bytes,
@@ -482,7 +483,7 @@ int mi_reduce_sum(long long n, const float *x, float *out, void *ws, size_t ws_b
     int count = (int)g;
     const float *pc = partials;
     void *args[] = {&pc, &count, &out};
-    return launch_raw(reinterpret_cast<const void *>(&reduce_final_kernel), 1, kReduceThreads,
+    return launch_raw(reinterpret_cast<const void *>(&reduce_final_kernel), 1, kFinalThreads,
                       args, s);
 }
 

@@ -54,16 +54,34 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partial_kernel(const fl
     if (threadIdx.x == 0) partials[blockIdx.x] = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
 }
 
-// out[0] = sum of the `count` partials (count may be 0), one workgroup.
-__global__ __launch_bounds__(kReduceThreads) void reduce_final_kernel(const float *__restrict__ partials,
-                                                                    int count, float *out) {
-    float s = 0.f;
-    for (int i = threadIdx.x; i < count; i += kReduceThreads) s += partials[i];
+// out[0] = sum of the `count` partials (0 <= count <= kFinalThreads *
+// kFinalPer), one workgroup of kFinalThreads.  Lane t loads partials t,
+// t + kFinalThreads, ... all at once (independent loads, one memory round
+// trip) and adds them in that order; the waves then add their lanes, and
+// wave 0 adds the per-wave sums.  The order is fixed, so the result is too.
+constexpr int kFinalThreads = 1024;
+constexpr int kFinalPer = 8;
+
+__global__ __launch_bounds__(kFinalThreads) void reduce_final_kernel(const float *__restrict__ partials,
+                                                                   int count, float *out) {
+    float v[kFinalPer];
+#pragma unroll
+    for (int j = 0; j < kFinalPer; ++j) {
+        const int i = threadIdx.x + j * kFinalThreads;
+        v[j] = i < count ? partials[i] : 0.f;
+    }
+    float s = v[0];
+#pragma unroll
+    for (int j = 1; j < kFinalPer; ++j) s += v[j];
     s = wave_sum(s);
-    __shared__ float wave_part[kReduceThreads / 64];
+    __shared__ float wave_part[kFinalThreads / 64];
     if ((threadIdx.x & 63) == 0) wave_part[threadIdx.x >> 6] = s;
     __syncthreads();
-    if (threadIdx.x == 0) out[0] = (wave_part[0] + wave_part[1]) + (wave_part[2] + wave_part[3]);
+    if (threadIdx.x < 64) {
+        float w = threadIdx.x < kFinalThreads / 64 ? wave_part[threadIdx.x] : 0.f;
+        w = wave_sum(w);
+        if (threadIdx.x == 0) out[0] = w;
+    }
 }
 
 }  // namespace mi
