@@ -1,0 +1,157 @@
+"""Edge cases at extreme sizes, and use under HIP graph capture.
+
+* Leading dimensions so large that a tile step's byte offsets leave the
+  31-bit range of a buffer load: the vector kernels then stage every step
+  through masked VGPR loads.  Checked bit-exact on integer operands, with
+  NaN in the (huge) pads.
+* Very tall or very wide products and a k of 2^24 (the largest k for which
+  an all-ones product is exact in float).
+* Calls captured into a HIP graph (through torch.cuda.graph) and replayed
+  several times, with eager work in between: every replay equals the eager
+  result.
+"""
+import numpy as np
+import pytest
+
+from parity import assert_exact
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import hpc_tiling_amd as hta
+else:
+    hta = None
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def ints(rng, shape):
+    return rng.integers(-3, 4, shape).astype(np.float32)
+
+
+def padded_device(values, ld):
+    """A rows x ld device tensor, NaN outside the logical block."""
+    rows, cols = values.shape
+    t = torch.full((rows, ld), float("nan"), device="cuda")
+    t[:, :cols] = torch.from_numpy(values).cuda()
+    return t
+
+
+def exact_product(Ah, Bh):
+    return (Ah.astype(np.int64) @ Bh.astype(np.int64)).astype(np.float32)
+
+
+@pytest.mark.parametrize("which", ["A", "B", "A^T"])
+def test_leading_dimension_beyond_direct_load_range(which):
+    """lda >= 2^31 / (4 * 64) floats for A (rows of a 64-row tile step span
+    more than 2^31 bytes), ldb >= 2^31 / (4 * 32) for B (32 k rows)."""
+    rng = np.random.default_rng(3)
+    m, n, k = 5, 70, 64
+    Ah, Bh = ints(rng, (m, k)), ints(rng, (k, n))
+    want = exact_product(Ah, Bh)
+    say("huge ld", which)
+    C = torch.zeros((m, n), device="cuda")
+    if which == "A":
+        A = padded_device(Ah, 9_000_000)[:, :k]
+        B = torch.from_numpy(Bh).cuda()
+    elif which == "B":
+        A = torch.from_numpy(Ah).cuda()
+        B = padded_device(Bh, 17_000_000)[:, :n]
+    else:  # A stored transposed (k x m) with a huge row stride
+        A = padded_device(np.ascontiguousarray(Ah.T), 17_000_000)[:, :m].t()
+        B = torch.from_numpy(Bh).cuda()
+    for config in (None, 6, 9):
+        C.zero_()
+        hta.sgemm(A, B, C, config=config)
+        torch.cuda.synchronize()
+        assert_exact(C.cpu().numpy(), want, f"huge ld {which} config {config}")
+    del A, B
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("shape", [(1_000_000, 8, 16), (8, 1_000_000, 16), (3, 3, 1_000_003)],
+                         ids=["tall", "wide", "long-k"])
+def test_extreme_aspect_ratios(shape):
+    m, n, k = shape
+    rng = np.random.default_rng(5)
+    Ah, Bh = ints(rng, (m, k)), ints(rng, (k, n))
+    say("aspect", shape)
+    want = exact_product(Ah, Bh)
+    A, B = torch.from_numpy(Ah).cuda(), torch.from_numpy(Bh).cuda()
+    C = torch.empty((m, n), device="cuda")
+    hta.sgemm(A, B, C)
+    torch.cuda.synchronize()
+    assert_exact(C.cpu().numpy(), want, f"mfma {shape}")
+    D = torch.empty((m, n), device="cuda")
+    hta.sgemm_splitk(A, B, D, splits=0)
+    torch.cuda.synchronize()
+    assert_exact(D.cpu().numpy(), want, f"splitk {shape}")
+
+
+def test_k_two_to_the_24_all_ones():
+    """2^24 is the largest count of ones a float sums exactly; both the
+    single-pass and split-K paths must reach it."""
+    k = 1 << 24
+    say("k=2^24")
+    A = torch.ones((2, k), device="cuda")
+    B = torch.ones((k, 3), device="cuda")
+    C = torch.empty((2, 3), device="cuda")
+    hta.sgemm(A, B, C)
+    D = torch.empty((2, 3), device="cuda")
+    hta.sgemm_splitk(A, B, D, splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(C, torch.full((2, 3), float(k), device="cuda"))
+    assert torch.equal(D, torch.full((2, 3), float(k), device="cuda"))
+
+
+def test_graph_capture_replay():
+    """mi_sgemm, mi_sgemm_splitk (with its workspace) and mi_reduce_sum
+    captured into one graph; inputs changed eagerly between replays."""
+    say("graph capture")
+    rng = np.random.default_rng(7)
+    m, n, k = 300, 200, 1000
+    A = torch.from_numpy(ints(rng, (m, k))).cuda()
+    B = torch.from_numpy(ints(rng, (k, n))).cuda()
+    C = torch.empty((m, n), device="cuda")
+    D = torch.empty((m, n), device="cuda")
+    x = torch.from_numpy(ints(rng, (1 << 20,)).reshape(-1)).cuda()
+    s = torch.empty(1, device="cuda")
+    ws = hta.splitk_workspace(m, n, k, 8)
+    rws = torch.empty(max(hta.mi_reduce_sum_workspace_bytes(x.numel()), 4), dtype=torch.uint8,
+                      device="cuda")
+    # first calls eagerly (the library checks the device once, outside capture)
+    hta.sgemm(A, B, C)
+    hta.sgemm_splitk(A, B, D, splits=8, workspace=ws)
+    hta.reduce_sum(x, out=s, workspace=rws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            hta.sgemm(A, B, C, 1.0, 0.0)
+            hta.sgemm_splitk(A, B, D, 1.0, 0.0, splits=8, workspace=ws)
+            hta.reduce_sum(x, out=s, workspace=rws)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        # eager work between replays: new inputs, and the outputs scribbled over
+        A.copy_(torch.from_numpy(ints(rng, (m, k))).cuda())
+        x.copy_(torch.from_numpy(ints(rng, (1 << 20,)).reshape(-1)).cuda())
+        C.fill_(float("nan"))
+        D.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = exact_product(A.cpu().numpy(), B.cpu().numpy())
+        assert_exact(C.cpu().numpy(), want, f"graph replay {rep} mfma")
+        assert_exact(D.cpu().numpy(), want, f"graph replay {rep} splitk")
+        assert s.item() == float(x.cpu().double().sum()), f"graph replay {rep} reduce"
