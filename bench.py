@@ -292,7 +292,7 @@ def main(argv=None):
         "bound": "mfma" if kind != "valu" else "alu",
         "kernel": dominant,
         "achieved": value,
-        "peak": (pm.PEAK_FP32_MFMA if kind != "valu" else pm.PEAK_FP32_VALU_SCALAR) / 1e12,
+        "peak": (pm.PEAK_FP32_MFMA if kind != "valu" else pm.PEAK_FP32_VECTOR) / 1e12,
         "unit": "TFLOP/s",
         "frac": None,
         "traffic": read_traffic(kind, w.name),

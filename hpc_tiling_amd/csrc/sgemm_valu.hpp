@@ -5,8 +5,12 @@
 // each thread accumulating an 8 x 8 block of C as 8 outer products of 8 A
 // values by 8 B values per k step (64 FMAs per "small iteration"; page
 // aerisun.top, section "Register Tiling 与线程内复用").  It is kept as a
-// measured comparison for the matrix-core path: on gfx950 a wave64 FP32 FMA
-// retires 128 FLOP per clock per CU, half the FP32 MFMA rate.
+// measured comparison for the matrix-core path.  Its bound is the FP32
+// vector peak (157.3 TFLOP/s on MI355X, the same as the FP32 matrix peak):
+// on gfx950 non-packed v_fmac_f32 with all operands in VGPRs retires more
+// than 128 FLOP per clock per CU (an outer-product loop without memory
+// sustains 115 TFLOP/s), although FMA chains with an SGPR operand stay at
+// 128.
 //
 // Layout on gfx950:
 //   * A is stored in LDS k-major (transposed while staging) so that a thread's
@@ -15,9 +19,16 @@
 //   * A thread owns rows {4ty..4ty+3} U {64+4ty..64+4ty+3} and the same split
 //     of columns with tx, so the 16 threads of a row group read 16
 //     consecutive float4 of B (no bank conflict) and broadcast A.
-//   * Global loads of step t+1 go to VGPRs before the FMAs of step t and to
-//     the other LDS buffer after them (page "gemm优化", section on prefetch).
+//   * Global loads run two k steps ahead through two register sets (page
+//     "gemm优化", section on prefetch, with one more step of distance): the
+//     tile of step t+2 is loaded before the FMAs of step t, and the tile of
+//     step t+1 (loaded a step earlier) goes to the other LDS buffer after
+//     them.  At 2048^3 each SIMD holds a single wave of this kernel, so the
+//     load latency must fit in the FMAs of a step or more: one step (2048
+//     FMA cycles) was not enough.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -50,29 +61,38 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
     const int br = tid >> 5, bc = 4 * (tid & 31);
     const float *asrc = p.A + (long long)(m0 + ar) * p.lda + ac;
     const float *bsrc = p.B + (long long)br * p.ldb + n0 + bc;
-    f32x4 ra, rb;
+    struct Regs {
+        f32x4 a, b;
+    };
+    Regs r0, r1;  // the staged tiles of two consecutive steps
 
-    auto load_step = [&](int step) {
+    auto load_step = [&](Regs &r, int step) {
         const int k0 = step * T::BK;
         const bool full_k = k0 + T::BK <= p.k;
         if (VEC && full_m && full_k) {
-            ra = *reinterpret_cast<const f32x4 *>(asrc + k0);
+            r.a = *reinterpret_cast<const f32x4 *>(asrc + k0);
         } else {
             const int valid = (m0 + ar < p.m) ? min(4, p.k - (k0 + ac)) : 0;
-            ra = load4_masked<VEC>(asrc + k0, valid);
+            r.a = load4_masked<VEC>(asrc + k0, valid);
         }
         const float *b = bsrc + (long long)k0 * p.ldb;
         if (VEC && full_n && full_k) {
-            rb = *reinterpret_cast<const f32x4 *>(b);
+            r.b = *reinterpret_cast<const f32x4 *>(b);
         } else {
             const int valid = (k0 + br < p.k) ? min(4, p.n - (n0 + bc)) : 0;
-            rb = load4_masked<VEC>(b, valid);
+            r.b = load4_masked<VEC>(b, valid);
         }
     };
-    auto store_step = [&](int buf) {
+    // Interior tile, all k of the step in range: plain 16-byte loads.
+    auto load_full = [&](Regs &r, int step) {
+        const int k0 = step * T::BK;
+        r.a = *reinterpret_cast<const f32x4 *>(asrc + k0);
+        r.b = *reinterpret_cast<const f32x4 *>(bsrc + (long long)k0 * p.ldb);
+    };
+    auto store_step = [&](const Regs &r, int buf) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) As[buf][(ac + c) * T::LDS_S + ar] = ra[c];
-        *reinterpret_cast<f32x4 *>(&Bs[buf][br * T::LDS_S + bc]) = rb;
+        for (int c = 0; c < 4; ++c) As[buf][(ac + c) * T::LDS_S + ar] = r.a[c];
+        *reinterpret_cast<f32x4 *>(&Bs[buf][br * T::LDS_S + bc]) = r.b;
     };
 
     float acc[T::RM][T::RN];
@@ -82,32 +102,72 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
         for (int j = 0; j < T::RN; ++j) acc[i][j] = 0.f;
 
     if (nsteps > 0) {
-        load_step(0);
-        store_step(0);
+        load_step(r0, 0);
+        if (nsteps > 1) load_step(r1, 1);
+        store_step(r0, 0);
         __syncthreads();
     }
-    for (int step = 0; step < nsteps; ++step) {
+    // Step `step` computes from LDS buffer step % 2.  On entry `cur` holds
+    // nothing live and `nxt` holds the tile of step+1; `cur` is refilled with
+    // the tile of step+2, and `nxt` is written to the other buffer.
+    // Fragments: the 8 A and 8 B values of one k, read one k ahead of the
+    // FMAs that use them (two sets); the fences keep the compiler from
+    // hoisting every read of a step to its top, which would hold 128 VGPRs.
+    struct Frag {
+        f32x4 a0, a1, b0, b1;
+    };
+    auto read_frag = [&](Frag &f, int buf, int kk) {
+        const float *arow = &As[buf][kk * T::LDS_S];
+        const float *brow = &Bs[buf][kk * T::LDS_S];
+        f.a0 = *reinterpret_cast<const f32x4 *>(arow + 4 * ty);
+        f.a1 = *reinterpret_cast<const f32x4 *>(arow + 64 + 4 * ty);
+        f.b0 = *reinterpret_cast<const f32x4 *>(brow + 4 * tx);
+        f.b1 = *reinterpret_cast<const f32x4 *>(brow + 64 + 4 * tx);
+    };
+    auto fma_block = [&](const Frag &f) {
+        const float av[8] = {f.a0[0], f.a0[1], f.a0[2], f.a0[3], f.a1[0], f.a1[1], f.a1[2], f.a1[3]};
+        const float bv[8] = {f.b0[0], f.b0[1], f.b0[2], f.b0[3], f.b1[0], f.b1[1], f.b1[2], f.b1[3]};
+#pragma unroll
+        for (int i = 0; i < T::RM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::RN; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+    };
+    // FULL: the steady state of an interior tile (the tile of step+2 exists
+    // and is whole), without any branch in the step.
+    auto one_step = [&](int step, Regs &cur, Regs &nxt, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const int buf = step & 1;
-        const bool more = step + 1 < nsteps;
-        if (more) load_step(step + 1);
+        if (FULL)
+            load_full(cur, step + 2);
+        else if (step + 2 < nsteps)
+            load_step(cur, step + 2);
+        Frag f[2];
+        read_frag(f[0], buf, 0);
 #pragma unroll
         for (int kk = 0; kk < T::BK; ++kk) {
-            const float *arow = &As[buf][kk * T::LDS_S];
-            const float *brow = &Bs[buf][kk * T::LDS_S];
-            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(arow + 4 * ty);
-            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(arow + 64 + 4 * ty);
-            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(brow + 4 * tx);
-            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(brow + 64 + 4 * tx);
-            const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-#pragma unroll
-            for (int i = 0; i < T::RM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::RN; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+            if (kk + 1 < T::BK) read_frag(f[(kk + 1) & 1], buf, kk + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            fma_block(f[kk & 1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) store_step(buf ^ 1);
+        if (FULL || step + 1 < nsteps) store_step(nxt, buf ^ 1);
         __syncthreads();
+    };
+    // Two steps per iteration, so the register sets alternate at compile
+    // time; the steady loop stops while the tile four steps ahead is whole.
+    int step = 0;
+    if (VEC && full_m && full_n) {
+        const int nfull = p.k / T::BK;
+        for (; step + 3 < nfull; step += 2) {
+            one_step(step, r0, r1, std::true_type{});
+            one_step(step + 1, r1, r0, std::true_type{});
+        }
     }
+    for (; step + 1 < nsteps; step += 2) {
+        one_step(step, r0, r1, std::false_type{});
+        one_step(step + 1, r1, r0, std::false_type{});
+    }
+    if (step < nsteps) one_step(step, r0, r1, std::false_type{});
 
     // Epilogue: row i of the micro tile is C row m0 + 4ty + i (i < 4) or
     // m0 + 64 + 4ty + i - 4; columns likewise with tx.

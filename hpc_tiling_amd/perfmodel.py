@@ -11,7 +11,11 @@ CUS = 256
 XCDS = 8
 PEAK_CLOCK_HZ = 2.4e9
 PEAK_FP32_MFMA = 157.3e12      # dense FP32 matrix, 256 FLOP/clk/CU at 2.4 GHz
-PEAK_FP32_VALU_SCALAR = 78.6e12  # wave64 v_fma_f32 without packed math: 128 FLOP/clk/CU
+PEAK_FP32_VECTOR = 157.3e12    # FP32 vector ALUs, 256 FLOP/clk/CU at 2.4 GHz
+# Measured on gfx950 with non-packed v_fmac_f32 only: independent FMA chains
+# with one operand in an SGPR sustain 76 TFLOP/s (128 FLOP/clk/CU), but the
+# register-only outer-product loop of the VALU GEMM sustains 115 TFLOP/s, so
+# the vector peak, not half of it, bounds the VALU kernel.
 PEAK_HBM_BYTES = 8.0e12        # HBM3E
 ELEM = 4                       # bytes per float
 

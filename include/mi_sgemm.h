@@ -107,8 +107,7 @@ int mi_sgemm_ex(int trans_a, int trans_b, int m, int n, int k, float alpha,
  * an 8 x 8 block of C updated by outer products of 8 A and 8 B values
  * (page aerisun.top, section "Register Tiling 与线程内复用"), with a
  * double-buffered LDS stage.  Same arguments, semantics and errors as
- * mi_sgemm.  Its peak is that of wave64 FP32 FMA without packed math, half
- * the FP32 matrix rate.
+ * mi_sgemm.  It is bound by the FP32 vector peak (non-packed FMA).
  */
 int mi_sgemm_valu(int m, int n, int k, float alpha,
                   const float *A, int lda, const float *B, int ldb,

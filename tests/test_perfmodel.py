@@ -63,5 +63,5 @@ def test_roofline_and_mi355x_ridge():
     assert pm.roofline(10.0, 2.0, 30.0) == 10.0
     assert pm.ridge(pm.PEAK_FP32_MFMA, pm.PEAK_HBM_BYTES) == pytest.approx(19.66, abs=0.01)
     assert pm.PEAK_FP32_MFMA == pytest.approx(pm.CUS * 256 * pm.PEAK_CLOCK_HZ, rel=0.01)
-    assert pm.PEAK_FP32_VALU_SCALAR == pytest.approx(pm.CUS * 128 * pm.PEAK_CLOCK_HZ, rel=0.01)
+    assert pm.PEAK_FP32_VECTOR == pytest.approx(pm.CUS * 256 * pm.PEAK_CLOCK_HZ, rel=0.01)
     assert pm.splitk_combine_bytes(512, 512, 64) == 4 * 512 * 512 * 65
