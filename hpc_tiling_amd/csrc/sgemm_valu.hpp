@@ -183,13 +183,14 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = p.alpha * acc[i][4 * h + j];
             if (p.c_vec && col + 3 < p.n) {
+                // C is touched once: nontemporal access.
                 f32x4 *dst = reinterpret_cast<f32x4 *>(crow + col);
                 if (p.beta != 0.f) {
-                    const f32x4 c = *dst;
+                    const f32x4 c = __builtin_nontemporal_load(dst);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) v[j] = __builtin_fmaf(p.beta, c[j], v[j]);
                 }
-                *dst = v;
+                __builtin_nontemporal_store(v, dst);
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
