@@ -155,3 +155,49 @@ def test_graph_capture_replay():
         assert_exact(C.cpu().numpy(), want, f"graph replay {rep} mfma")
         assert_exact(D.cpu().numpy(), want, f"graph replay {rep} splitk")
         assert s.item() == float(x.cpu().double().sum()), f"graph replay {rep} reduce"
+
+
+def test_concurrent_host_threads_and_streams():
+    """Four host threads, each with its own stream and workspace, call the
+    library at the same time (ctypes releases the GIL around each call); the
+    library holds no per-call global state, so every result is exact."""
+    import threading
+    say("threads x streams")
+    rng = np.random.default_rng(13)
+    shapes = [(300, 200, 257), (129, 511, 64), (64, 64, 4096), (1000, 33, 100)]
+    cases = []
+    for (m, n, k) in shapes:
+        Ah, Bh = ints(rng, (m, k)), ints(rng, (k, n))
+        cases.append((torch.from_numpy(Ah).cuda(), torch.from_numpy(Bh).cuda(), exact_product(Ah, Bh)))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(idx):
+        try:
+            A, B, want = cases[idx]
+            m, n, k = A.shape[0], B.shape[1], A.shape[1]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                ws = hta.splitk_workspace(m, n, k, 3)
+                outs = []
+                for rep in range(10):
+                    C = torch.empty((m, n), device="cuda")
+                    if rep % 2:
+                        hta.sgemm_splitk(A, B, C, splits=3, workspace=ws)
+                    else:
+                        hta.sgemm(A, B, C)
+                    outs.append(C)
+            stream.synchronize()
+            for rep, C in enumerate(outs):
+                if not np.array_equal(C.cpu().numpy(), want):
+                    errors.append(f"thread {idx} call {rep} differs")
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(f"thread {idx}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
