@@ -114,51 +114,104 @@ int choose_mfma_config(int m, int n, int k) {
     return best;
 }
 
-// Tile configuration of the split-K partial kernel: the 128 x 128 x 32,
-// 16-wave tile when C holds at least a few of them (slices then supply the
-// parallelism), smaller tiles for small C.  Measured on MI355X at 512 x 512 x
-// 262144 with one round of workgroups: 143.5 TFLOP/s (16 slices).
-int choose_split_config(int m, int n, int k) {
-    (void)k;
-    if (tile_count(m, n, 9) >= 4) return 9;  // 128 x 128 x 32, 16 waves
-    if (tile_count(m, n, 8) >= 4) return 8;  // 128 x 64 x 32, 4 waves
-    return 6;                                // 64 x 64 x 32, 4 waves
-}
-
 // ---------------------------------------------------------------------------
-// Split-K sizing.
+// Split-K planning.
 // ---------------------------------------------------------------------------
 struct SplitPlan {
-    int splits;        // slices actually used
+    int config;        // tile configuration of the partial (or full-k) kernel
+    int splits;        // slices actually used (1: the full-k kernel, no workspace)
     int k_per_split;   // multiple of the k step
     long long slice;   // floats per workspace slice
-    size_t bytes;      // workspace bytes including alignment slack
+    size_t bytes;      // workspace bytes including alignment slack (0 for one slice)
 };
 
 constexpr size_t kWsAlign = 256;
 
-SplitPlan plan_split(int m, int n, int k, int splits, int config) {
-    SplitPlan sp{0, 0, 0, 0};
+// Slices of k for a request of `want` (>= 1): whole k steps per slice; the
+// slice count that results may be smaller than asked.
+SplitPlan make_plan(int m, int n, int k, long long want, int config) {
+    SplitPlan sp{config, 0, 0, 0, 0};
     if (m <= 0 || n <= 0 || k <= 0) return sp;
     const MfmaConfig &c = kMfmaConfigs[config];
-    const long long tiles = ceil_div(m, c.bm) * ceil_div(n, c.bn);
-    long long want = splits;
-    if (want == 0) {
-        // One round of workgroups (one per CU), with slices of at least 8 k
-        // steps.
-        const long long target_wg = kCUs;
-        want = ceil_div(target_wg, tiles);
-        const long long max_by_k = ceil_div(k, 8LL * c.bk);
-        if (want > max_by_k) want = max_by_k;
-        if (want > 256) want = 256;
-        if (want < 1) want = 1;
-    }
-    long long kps = ceil_div(ceil_div(k, want), c.bk) * c.bk;
+    const long long kps = ceil_div(ceil_div(k, want), c.bk) * c.bk;
     sp.k_per_split = (int)kps;
     sp.splits = (int)ceil_div(k, kps);
+    if (sp.splits == 1) sp.k_per_split = k;
     sp.slice = ceil_div((long long)m * n, 64) * 64;
-    sp.bytes = (size_t)sp.splits * (size_t)sp.slice * sizeof(float) + kWsAlign;
+    sp.bytes = sp.splits > 1 ? (size_t)sp.splits * (size_t)sp.slice * sizeof(float) + kWsAlign : 0;
     return sp;
+}
+
+// Modelled time (us) of a split plan.  Workgroups spread evenly over the
+// CUs; the busiest CU runs ceil(tiles * S / CUs) of them, each for its k
+// steps at the configuration's efficiency plus a fixed prologue / epilogue
+// cost (divided among the workgroups one CU holds at once).  More than one
+// slice adds the combine: a launch and 4 m n (S + 1) bytes at HBM speed.
+// The constants are MI355X measurements: 2.4 GHz, ~3 us of prologue and
+// epilogue per workgroup, ~3 us of fixed combine cost, ~6 TB/s.
+constexpr double kClockMHz = 2400.0;
+constexpr double kWorkgroupOverheadUs = 3.0;
+constexpr double kCombineFixedUs = 3.0;
+constexpr double kCombineBytesPerUs = 6.0e6;
+constexpr size_t kAutoWorkspaceCap = size_t(512) << 20;  // automatic plans stay below this
+
+double split_cost_us(int m, int n, const SplitPlan &sp, double efficiency) {
+    const MfmaConfig &c = kMfmaConfigs[sp.config];
+    const long long lds = 3LL * (c.bm * c.bk + c.bk * c.bn) * 4;
+    const long long waves = (long long)c.wgm * c.wgn;
+    long long resident = (160LL * 1024) / lds;
+    if (resident > 32 / waves) resident = 32 / waves;
+    if (resident < 1) resident = 1;
+    const long long per_cu = ceil_div(tile_count(m, n, sp.config) * sp.splits, kCUs);
+    const double step_us = 2.0 * c.bm * c.bn * c.bk / 256.0 / efficiency / kClockMHz;
+    double t = (double)per_cu *
+               ((double)ceil_div(sp.k_per_split, c.bk) * step_us + kWorkgroupOverheadUs / resident);
+    if (sp.splits > 1)
+        t += kCombineFixedUs + 4.0 * (double)m * n * (sp.splits + 1) / kCombineBytesPerUs;
+    return t;
+}
+
+double config_efficiency(int id) {
+    for (const Candidate &cand : kCandidates)
+        if (cand.id == id) return cand.efficiency;
+    return 0.9;
+}
+
+// The split plan for a call: `splits` > 0 fixes the slice count (rounded to
+// whole k steps), 0 lets the model choose it; `config` >= 0 fixes the tile
+// configuration.  A plan of one slice runs the full-k kernel, and then (when
+// the configuration is free) with the tiles mi_sgemm would choose.  Measured
+// on MI355X at 512 x 512 x 262144: 16 slices of the 128 x 128 x 32 tile, one
+// round of 256 workgroups.
+SplitPlan plan_split(int m, int n, int k, int splits, int config) {
+    if (m <= 0 || n <= 0 || k <= 0) return SplitPlan{config < 0 ? 0 : config, 0, 0, 0, 0};
+    SplitPlan best{};
+    double best_cost = 0.0;
+    bool have = false;
+    auto consider = [&](int id, long long want) {
+        const SplitPlan sp = make_plan(m, n, k, want, id);
+        if (splits == 0 && sp.bytes > kAutoWorkspaceCap) return;
+        const double cost = split_cost_us(m, n, sp, config_efficiency(id));
+        if (!have || cost < best_cost * 0.99) {
+            best = sp;
+            best_cost = cost;
+            have = true;
+        }
+    };
+    for (const Candidate &cand : kCandidates) {
+        const int id = cand.id;
+        if (config >= 0 && id != config) continue;
+        if (splits > 0) {
+            consider(id, splits);
+            continue;
+        }
+        const long long ksteps = ceil_div(k, kMfmaConfigs[id].bk);
+        for (long long want = 1; want <= 256 && want <= ksteps; want += (want < 32 ? 1 : 4))
+            consider(id, want);
+    }
+    if (!have) best = make_plan(m, n, k, splits > 0 ? splits : 1, config);  // forced non-candidate
+    if (best.splits == 1 && config < 0) best.config = choose_mfma_config(m, n, k);
+    return best;
 }
 
 // ---------------------------------------------------------------------------
@@ -257,6 +310,17 @@ int prologue(int m, int n, int k, float alpha, const float *A, int lda, const fl
     return MI_SGEMM_SUCCESS;
 }
 
+// The full-k matrix-core kernel of configuration `id` (arguments checked).
+int launch_full(int id, int ta, int tb, int m, int n, int k, float alpha, const float *A, int lda,
+                const float *B, int ldb, float beta, float *C, int ldc, hipStream_t s) {
+    const MfmaConfig &c = kMfmaConfigs[id];
+    GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
+    a.tiles_m = (int)ceil_div(m, c.bm);
+    a.tiles_n = (int)ceil_div(n, c.bn);
+    const long long grid = (long long)a.tiles_m * a.tiles_n;
+    return launch(c.full[ta][tb][vector_ok(A, lda, B, ldb)], grid, 64 * c.wgm * c.wgn, s, a);
+}
+
 int run_mfma(int config, int ta, int tb, int m, int n, int k, float alpha, const float *A,
              int lda, const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
     if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
@@ -265,12 +329,7 @@ int run_mfma(int config, int ta, int tb, int m, int n, int k, float alpha, const
     int st = prologue(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, &done, ta, tb);
     if (st || done) return st;
     const int id = config < 0 ? choose_mfma_config(m, n, k) : config;
-    const MfmaConfig &c = kMfmaConfigs[id];
-    GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
-    a.tiles_m = (int)ceil_div(m, c.bm);
-    a.tiles_n = (int)ceil_div(n, c.bn);
-    const long long grid = (long long)a.tiles_m * a.tiles_n;
-    return launch(c.full[ta][tb][vector_ok(A, lda, B, ldb)], grid, 64 * c.wgm * c.wgn, s, a);
+    return launch_full(id, ta, tb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s);
 }
 
 int run_valu(int config, int m, int n, int k, float alpha, const float *A, int lda,
@@ -303,11 +362,14 @@ int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, con
         st = check_device();
         return st ? st : launch_scale(m, n, beta, C, ldc, s);
     }
-    const int id = config < 0 ? choose_split_config(m, n, k) : config;
-    const SplitPlan sp = plan_split(m, n, k, splits, id);
-    if (!ws || ws_bytes < sp.bytes) return MI_SGEMM_ERROR_WORKSPACE;
+    const SplitPlan sp = plan_split(m, n, k, splits, config);
+    if (sp.bytes > 0 && (!ws || ws_bytes < sp.bytes)) return MI_SGEMM_ERROR_WORKSPACE;
     st = check_device();
     if (st) return st;
+    const int id = sp.config;
+    // one slice: the full-k kernel, no workspace (the same sums and rounding
+    // as the partial-plus-combine path would give)
+    if (sp.splits == 1) return launch_full(id, ta, tb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s);
 
     float *wsa = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + kWsAlign - 1) &
                                            ~(uintptr_t)(kWsAlign - 1));
@@ -346,8 +408,9 @@ int run_splitk_atomic(int config, int m, int n, int k, float alpha, const float 
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (k == 0 || alpha == 0.f) return launch_scale(m, n, beta, C, ldc, s);
-    const int id = config < 0 ? choose_split_config(m, n, k) : config;
-    const SplitPlan sp = plan_split(m, n, k, splits, id);
+    const SplitPlan sp = plan_split(m, n, k, splits, config);
+    const int id = sp.config;
+    if (sp.splits == 1) return launch_full(id, 0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s);
     if (beta != 1.f) {
         st = launch_scale(m, n, beta, C, ldc, s);
         if (st) return st;
@@ -443,8 +506,7 @@ int mi_sgemm_splitk_atomic(int m, int n, int k, float alpha, const float *A, int
 size_t mi_sgemm_splitk_with_config_workspace_bytes(int config, int m, int n, int k, int splits) {
     if (m < 0 || n < 0 || k < 0 || splits < 0 || splits > k || config >= kNumMfmaConfigs)
         return 0;
-    const int id = config < 0 ? choose_split_config(m, n, k) : config;
-    return plan_split(m, n, k, splits, id).bytes;
+    return plan_split(m, n, k, splits, config).bytes;
 }
 
 size_t mi_reduce_sum_workspace_bytes(long long n) {
@@ -530,10 +592,13 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
                kernel == MI_SGEMM_KERNEL_SPLITK_ATOMIC) {
         int id;
         const bool split = kernel != MI_SGEMM_KERNEL_MFMA;
+        SplitPlan sp{};
         if (split) {
             if (config >= kNumMfmaConfigs || splits < 0 || splits > k)
                 return MI_SGEMM_ERROR_INVALID_VALUE;
-            id = config < 0 ? choose_split_config(m, n, k) : config;
+            sp = plan_split(m, n, k, splits, config);
+            id = (m > 0 && n > 0 && k > 0) ? sp.config
+                                           : (config < 0 ? choose_mfma_config(m, n, k) : config);
         } else {
             if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
             id = config < 0 ? choose_mfma_config(m, n, k) : config;
@@ -547,7 +612,6 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
         plan->fma_per_small_iteration = (plan->micro_m / 32) * (plan->micro_n / 32);
         plan->outputs_per_thread = plan->micro_m * plan->micro_n / 64;
         if (split) {
-            const SplitPlan sp = plan_split(m, n, k, splits, id);
             plan->splits = sp.splits;
             plan->k_per_split = sp.k_per_split;
             plan->workspace_bytes = kernel == MI_SGEMM_KERNEL_SPLITK ? sp.bytes : 0;

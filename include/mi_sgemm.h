@@ -117,8 +117,8 @@ int mi_sgemm_valu(int m, int n, int k, float alpha,
  * mi_sgemm_splitk_workspace_bytes -- bytes of device workspace that
  * mi_sgemm_splitk needs for these sizes and this split request (splits = 0
  * asks the library to choose).  Returns 0 when no workspace is needed
- * (m == 0, n == 0 or k == 0) and also for invalid arguments (m, n, k < 0,
- * splits < 0 or splits > k).
+ * (m == 0, n == 0 or k == 0, or a plan of one slice) and also for invalid
+ * arguments (m, n, k < 0, splits < 0 or splits > k).
  */
 size_t mi_sgemm_splitk_workspace_bytes(int m, int n, int k, int splits);
 
@@ -130,11 +130,16 @@ size_t mi_sgemm_splitk_workspace_bytes(int m, int n, int k, int splits);
  * partials of every C element -- each lane summing some slices, then a
  * cross-lane wavefront reduction (page aerisun.top, sections
  * "先在线程内累加，再交换部分和" and "Warp shuffle 的数据交换") -- and applies
- * alpha and beta.  splits: requested S (0 = choose automatically; the
- * library may use fewer slices so that each is a whole number of k steps).
- * ws / ws_bytes: caller-owned device workspace of at least
- * mi_sgemm_splitk_workspace_bytes(m, n, k, splits) bytes, 256-byte aligned
- * for best speed; its contents on return are unspecified.  Two calls that
+ * alpha and beta.  splits: requested S (the library may use fewer slices
+ * so that each is a whole number of k steps), or 0: the library chooses the
+ * tile configuration and S with a time model of MI355X (workgroup rounds
+ * over the 256 CUs, per-workgroup overhead, the combine's cost), keeping
+ * the workspace under 512 MiB.  A plan of one slice runs the single-pass
+ * kernel directly, with the same result as mi_sgemm_ex, and needs no
+ * workspace (ws may then be NULL).  ws / ws_bytes: caller-owned device
+ * workspace of at least mi_sgemm_splitk_workspace_bytes(m, n, k, splits)
+ * bytes, 256-byte aligned for best speed; its contents on return are
+ * unspecified.  Two calls that
  * share a workspace must be ordered on one stream.  Other arguments and
  * errors as mi_sgemm, plus MI_SGEMM_ERROR_WORKSPACE.
  */
