@@ -81,6 +81,8 @@ struct Operand {
     static constexpr int ROWS = KROWS ? T::BK : E;         // LDS tile rows
     static constexpr int CH = KROWS ? E / 4 : T::BK / 4;   // 16-byte chunks per row
     static constexpr int PER = ROWS * CH / T::NT;          // chunks per thread per step
+    static constexpr int ROW_WORDS = 4 * CH;               // floats per LDS row
+    static constexpr int PER4 = ROWS * ROW_WORDS / T::NT;  // 4-byte direct loads per lane per step
     static constexpr int ELEMS = E * T::BK;
     using Frag = std::conditional_t<KROWS, Vals4, f32x4>;  // four k values of one lane
     static_assert(KROWS ? E % 64 == 0 : (T::BK == 16 || T::BK == 32),
@@ -113,6 +115,16 @@ struct Operand {
     __device__ static int direct_offset(int row, int c, long long ld, int lim) {
         return KROWS ? (int)(4 * ((long long)row * ld + 4 * min(c, lim)))
                      : (int)(4 * ((long long)min(row, lim) * ld + 4 * c));
+    }
+    // 4-byte direct loads (operands not 16-byte aligned): word w of the
+    // swizzled LDS tile is loaded from the element the layout puts there (the
+    // chunk swizzle undone), e clamped to e_last.  The lanes of one load cover
+    // one or two row segments, only in permuted chunk order.
+    __device__ static int word_offset(int w, long long ld, int e_last) {
+        const int r = w / ROW_WORDS, u = w % ROW_WORDS;
+        const int col = 4 * ((u >> 2) ^ swz(r)) + (u & 3);
+        return KROWS ? (int)(4 * ((long long)r * ld + min(col, e_last)))
+                     : (int)(4 * ((long long)min(r, e_last) * ld + col));
     }
     // Direct loads need every byte offset of a tile to fit the 31-bit range.
     __device__ static bool direct_fits(long long ld) {
@@ -172,6 +184,14 @@ __device__ __forceinline__ void load_lds16(const float *base, float *lds, int vo
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, 0x7fffffff,
                                                         kBufferWord3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds), 16, voffset, 0, 0, 0);
+}
+
+// The same with buffer_load_dword ... lds: 4 bytes per lane into LDS at
+// lds + 4 * lane.
+__device__ __forceinline__ void load_lds4(const float *base, float *lds, int voffset) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, 0x7fffffff,
+                                                        kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds), 4, voffset, 0, 0, 0);
 }
 
 // Epilogue modes.  kFull: the whole k range, C = alpha*acc + beta*C.
@@ -238,15 +258,16 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     const int kbeg = SPLIT ? slice * p.k_per_split : 0;
     const int kend = SPLIT ? min(p.k, kbeg + p.k_per_split) : p.k;
     const int nsteps = (kend - kbeg + T::BK - 1) / T::BK;
-    // Whole k steps of aligned operands are loaded directly into LDS (byte
-    // offsets inside one tile step must fit the 31-bit buffer offset).  On
-    // the m / n edge, rows or chunks past the edge are clamped to the last
-    // valid one: they only feed outputs that are never stored, and every
-    // address stays inside the operands.
-    const bool direct_ok = VEC && OA::direct_fits(p.lda) && OB::direct_fits(p.ldb);
+    // Whole k steps are loaded directly into LDS (byte offsets inside one
+    // tile step must fit the 31-bit buffer offset): 16 bytes per lane for
+    // aligned operands, 4 bytes otherwise.  On the m / n edge, rows, chunks
+    // or elements past the edge are clamped to the last valid one: they only
+    // feed outputs that are never stored, and every address stays inside the
+    // operands.
+    const bool direct_ok = OA::direct_fits(p.lda) && OB::direct_fits(p.ldb);
     const int ndirect = direct_ok ? (kend - kbeg) / T::BK : 0;
-    const int a_lim = OA::clamp_limit(min(T::BM, p.m - m0));
-    const int b_lim = OB::clamp_limit(min(T::BN, p.n - n0));
+    const int a_lim = VEC ? OA::clamp_limit(min(T::BM, p.m - m0)) : min(T::BM, p.m - m0) - 1;
+    const int b_lim = VEC ? OB::clamp_limit(min(T::BN, p.n - n0)) : min(T::BN, p.n - n0) - 1;
     const float *Ablk = OA::block_base(p.A, p.lda, m0);
     const float *Bblk = OB::block_base(p.B, p.ldb, n0);
 
@@ -261,17 +282,31 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
         const int k0 = kbeg + step * T::BK;
         const float *abase = OA::tile_base(Ablk, p.lda, k0);
         const float *bbase = OB::tile_base(Bblk, p.ldb, k0);
+        if constexpr (VEC) {
 #pragma unroll
-        for (int i = 0; i < OA::PER; ++i) {
-            int row, c;
-            OA::chunk(tid, i, row, c);
-            load_lds16(abase, as + (i * T::WAVES + wave) * 256, OA::direct_offset(row, c, p.lda, a_lim));
-        }
+            for (int i = 0; i < OA::PER; ++i) {
+                int row, c;
+                OA::chunk(tid, i, row, c);
+                load_lds16(abase, as + (i * T::WAVES + wave) * 256, OA::direct_offset(row, c, p.lda, a_lim));
+            }
 #pragma unroll
-        for (int i = 0; i < OB::PER; ++i) {
-            int row, c;
-            OB::chunk(tid, i, row, c);
-            load_lds16(bbase, bs + (i * T::WAVES + wave) * 256, OB::direct_offset(row, c, p.ldb, b_lim));
+            for (int i = 0; i < OB::PER; ++i) {
+                int row, c;
+                OB::chunk(tid, i, row, c);
+                load_lds16(bbase, bs + (i * T::WAVES + wave) * 256, OB::direct_offset(row, c, p.ldb, b_lim));
+            }
+        } else {
+            // 64-word window `win` of the tile is filled by one wave's load
+#pragma unroll
+            for (int i = 0; i < OA::PER4; ++i) {
+                const int win = i * T::WAVES + wave;
+                load_lds4(abase, as + win * 64, OA::word_offset(win * 64 + lane, p.lda, a_lim));
+            }
+#pragma unroll
+            for (int i = 0; i < OB::PER4; ++i) {
+                const int win = i * T::WAVES + wave;
+                load_lds4(bbase, bs + win * 64, OB::word_offset(win * 64 + lane, p.ldb, b_lim));
+            }
         }
     };
 

@@ -17,9 +17,10 @@
  * BLAS op(X) = X^T): trans_a = 1 means A is stored k x m, A_it = A[t*lda + i]
  * with lda >= max(1, m); trans_b = 1 means B is stored n x k,
  * B_tj = B[j*ldb + t] with ldb >= max(1, k).  Column-major operands are the
- * transposed row-major ones, so every BLAS storage order is covered.  Pointers need no particular alignment and ld values need
- * not be multiples of 4: 16-byte vector loads are used when A and B are
- * 16-byte aligned with lda and ldb multiples of 4, element loads otherwise.
+ * transposed row-major ones, so every BLAS storage order is covered.  Pointers need no particular alignment (beyond that of a
+ * float) and ld values need not be multiples of 4: tiles of A and B move to
+ * on-chip memory 16 bytes per lane when both are 16-byte aligned with lda
+ * and ldb multiples of 4, and 4 bytes per lane otherwise.
  *
  * Memory and streams.  A, B, C and the workspace are device memory owned by
  * the caller; the library never allocates or frees memory in these calls.
