@@ -517,7 +517,8 @@ size_t mi_reduce_sum_workspace_bytes(long long n) {
 long long mi_reduce_sum_max_additions(long long n) {
     if (n <= 0) return 0;
     const long long g = reduce_grid(n);
-    const long long per_acc = ceil_div(ceil_div(n, 4), g * kReduceThreads);  // float4s per lane
+    // groups of four per lane: workgroups take ceil(groups / g) each
+    const long long per_acc = ceil_div(ceil_div(n >> 2, g), kReduceThreads);
     // per accumulator (+1 for a trailing element), 2 levels over the four
     // accumulators, 6 in the wave, 2 over the waves; then the final pass:
     // kFinalPer - 1 in a lane, 6 in the wave, 6 over the per-wave sums.
@@ -536,7 +537,8 @@ int mi_reduce_sum(long long n, const float *x, float *out, void *ws, size_t ws_b
     float *partials = static_cast<float *>(ws);
     if (g > 0) {
         const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
-        void *args[] = {&x, &n, &partials};
+        long long per = ceil_div(n >> 2, g);  // groups of four per workgroup
+        void *args[] = {&x, &n, &per, &partials};
         st = launch_raw(vec ? reinterpret_cast<const void *>(&reduce_partial_kernel<true>)
                             : reinterpret_cast<const void *>(&reduce_partial_kernel<false>),
                         g, kReduceThreads, args, s);
