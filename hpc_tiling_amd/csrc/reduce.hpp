@@ -1,6 +1,7 @@
 // reduce.hpp -- sum of a float array (page aerisun.top, section
 // "Reduce 的分层归约"): every lane first accumulates many inputs in registers
-// (grid-stride loop, section "先在线程内累加，再交换部分和"), then the wave
+// (section "先在线程内累加，再交换部分和"; here a contiguous run of the input per
+// workgroup, its lanes striding through it), then the wave
 // adds its lanes with register exchanges instead of LDS (section
 // "Warp shuffle 的数据交换", on wave64 with DPP rotations and row swaps), the
 // four waves of a workgroup meet in LDS, and a second single-workgroup kernel

@@ -5,12 +5,13 @@
 //   * a workgroup of WGM x WGN waves owns a BM x BN tile of C and walks k in
 //     steps of BK ("big iterations");
 //   * each step stages a BM x BK tile of A and a BK x BN tile of B in one of
-//     three LDS buffers.  Whole k steps of aligned operands use gfx950's
-//     direct global->LDS loads (buffer_load_dwordx4 ... lds: 16 bytes per
-//     lane, no VGPRs involved), issued two steps ahead; the partial last k
-//     step and unaligned operands use 16-byte (or element) loads through
-//     VGPRs with out-of-range elements stored as zeros (page aerisun.top,
-//     section "Shared Tiling 与 block 内复用");
+//     three LDS buffers.  Whole k steps use gfx950's direct global->LDS
+//     loads (buffer_load_dwordx4 ... lds, 16 bytes per lane, for aligned
+//     operands; buffer_load_dword ... lds, 4 bytes per lane, otherwise; no
+//     VGPRs involved), issued two steps ahead; the partial last k step (and
+//     tiles whose byte offsets exceed the buffer range) use masked 16-byte
+//     or element loads through VGPRs with out-of-range elements stored as
+//     zeros (page aerisun.top, section "Shared Tiling 与 block 内复用");
 //   * each wave owns a (BM/WGM) x (BN/WGN) sub-tile held as 32 x 32 blocks
 //     of v_mfma_f32_32x32x2_f32 accumulators and reads its A and B fragments
 //     from LDS one group of 8 k ahead of the MFMAs that use them.
