@@ -94,7 +94,7 @@ def check(orc, kind, w, ta, tb, integer, rows=None):
 
 
 # ---------------------------------------------------------------------------
-# Small ragged shapes, every tile configuration, vector and element loads
+# Small ragged shapes, every tile configuration, 16-byte and 4-byte loads
 # ---------------------------------------------------------------------------
 KINDS = (["mfma", "splitk", "splitk3"] + [f"mfma_cfg{i}" for i in range(N_MFMA_CFG)]
          + [f"splitk_cfg{i}" for i in range(N_MFMA_CFG)])
@@ -170,7 +170,7 @@ def test_workload_splitk_transposed(orc, combo, integer):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("kind", ["mfma", "splitk"])
 def test_misaligned_transposed(kind):
-    """Transposed operands one float off 16-byte alignment (element loads)."""
+    """Transposed operands one float off 16-byte alignment (4-byte loads)."""
     say("misaligned transposed", kind)
     m, n, k = 97, 131, 203
     rng = np.random.default_rng(7)
