@@ -156,12 +156,15 @@ def cpu_baseline(w, host, budget_s):
     nrows = int(min(w.m, max(len(probe), budget_s / max(per_row, 1e-9))))
     nrows = max(threads, (nrows // threads) * threads) if nrows < w.m else w.m
     rows = synth.sample_rows([w.wid, 4321], w.m, nrows)
-    # when every row fits the budget, whole passes are repeated to fill it
-    passes = 1 if nrows < w.m else int(max(1, min(50, budget_s / max(per_row * w.m, 1e-9))))
+    # when every row fits the budget, whole passes are repeated until it is spent
+    passes = 0
     t0 = time.perf_counter()
-    for _ in range(passes):
+    while True:
         orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc, rows=rows,
                   want_g=True, threads=threads)
+        passes += 1
+        if nrows < w.m or time.perf_counter() - t0 >= budget_s or passes >= 200:
+            break
     dt = time.perf_counter() - t0
     used = int(min(threads, len(rows)))
     flops = 2.0 * passes * len(rows) * w.n * w.k
