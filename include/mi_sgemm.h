@@ -17,10 +17,11 @@
  * BLAS op(X) = X^T): trans_a = 1 means A is stored k x m, A_it = A[t*lda + i]
  * with lda >= max(1, m); trans_b = 1 means B is stored n x k,
  * B_tj = B[j*ldb + t] with ldb >= max(1, k).  Column-major operands are the
- * transposed row-major ones, so every BLAS storage order is covered.  Pointers need no particular alignment (beyond that of a
- * float) and ld values need not be multiples of 4: tiles of A and B move to
- * on-chip memory 16 bytes per lane when both are 16-byte aligned with lda
- * and ldb multiples of 4, and 4 bytes per lane otherwise.
+ * transposed row-major ones, so every BLAS storage order is covered.
+ * Pointers need no particular alignment (beyond that of a float) and ld
+ * values need not be multiples of 4: tiles of A and B move to on-chip memory
+ * 16 bytes per lane when both are 16-byte aligned with lda and ldb multiples
+ * of 4, and 4 bytes per lane otherwise.
  *
  * Memory and streams.  A, B, C and the workspace are device memory owned by
  * the caller; the library never allocates or frees memory in these calls.
@@ -140,9 +141,9 @@ size_t mi_sgemm_splitk_workspace_bytes(int m, int n, int k, int splits);
  * workspace (ws may then be NULL).  ws / ws_bytes: caller-owned device
  * workspace of at least mi_sgemm_splitk_workspace_bytes(m, n, k, splits)
  * bytes, 256-byte aligned for best speed; its contents on return are
- * unspecified.  Two calls that
- * share a workspace must be ordered on one stream.  Other arguments and
- * errors as mi_sgemm, plus MI_SGEMM_ERROR_WORKSPACE.
+ * unspecified.  Two calls that share a workspace must be ordered on one
+ * stream.  Other arguments and errors as mi_sgemm, plus
+ * MI_SGEMM_ERROR_WORKSPACE.
  */
 int mi_sgemm_splitk(int m, int n, int k, float alpha,
                     const float *A, int lda, const float *B, int ldb,
