@@ -252,11 +252,21 @@ def _operand(t, name):
     return p, ld
 
 
-def _stream(stream):
+def _stream(stream, device=None):
     import torch
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _device_of(*tensors):
+    """The one device all given tensors (None skipped) live on.  The library
+    launches on the current device, so the helpers make this one current
+    around each call; tensors on different devices are refused."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"tensors are on different devices: {sorted(str(d) for d in devs)}")
+    return devs.pop()
 
 
 def _output(A, B, C, beta):
@@ -301,13 +311,16 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
     A (m x k), B (k x n), C (m x n): float32 device tensors, each row-major
     or column-major (a transposed view such as ``X.t()`` is passed as the
     transposed operand, without a copy)."""
+    import torch
     (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc = _prepare_ex(A, B, C, beta)
-    s = _stream(stream)
-    if config is None:
-        st = lib.mi_sgemm_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, s)
-    else:
-        st = lib.mi_sgemm_with_config(KERNEL_MFMA, config, ta, tb, m, n, k, alpha, pa, lda, pb,
-                                      ldb, beta, pc, ldc, s)
+    dev = _device_of(A, B, C)
+    with torch.cuda.device(dev):
+        s = _stream(stream, dev)
+        if config is None:
+            st = lib.mi_sgemm_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, s)
+        else:
+            st = lib.mi_sgemm_with_config(KERNEL_MFMA, config, ta, tb, m, n, k, alpha, pa, lda,
+                                          pb, ldb, beta, pc, ldc, s)
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_ex")
     return C
@@ -316,8 +329,12 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
 def sgemm_valu(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
     """Same as sgemm (row-major operands only), on the register-tiled VALU
     kernel."""
+    import torch
     m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
-    st = lib.mi_sgemm_valu(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, _stream(stream))
+    dev = _device_of(A, B, C)
+    with torch.cuda.device(dev):
+        st = lib.mi_sgemm_valu(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
+                               _stream(stream, dev))
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_valu")
     return C
@@ -339,17 +356,21 @@ def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, st
     """Same as sgemm with the k range split into slices; `workspace` is a
     device tensor of at least mi_sgemm_splitk_workspace_bytes bytes (allocated
     here when None).  `config` forces the partial kernel's tile configuration."""
+    import torch
     (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc = _prepare_ex(A, B, C, beta)
     if workspace is None:
         workspace = splitk_workspace(m, n, k, splits, device=A.device, config=config)
+    dev = _device_of(A, B, C, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
-    if config is None:
-        st = lib.mi_sgemm_splitk_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
-                                    splits, workspace.data_ptr(), ws_bytes, _stream(stream))
-    else:
-        st = lib.mi_sgemm_splitk_with_config(config, ta, tb, m, n, k, alpha, pa, lda, pb, ldb,
-                                             beta, pc, ldc, splits, workspace.data_ptr(),
-                                             ws_bytes, _stream(stream))
+    with torch.cuda.device(dev):
+        s = _stream(stream, dev)
+        if config is None:
+            st = lib.mi_sgemm_splitk_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
+                                        splits, workspace.data_ptr(), ws_bytes, s)
+        else:
+            st = lib.mi_sgemm_splitk_with_config(config, ta, tb, m, n, k, alpha, pa, lda, pb,
+                                                 ldb, beta, pc, ldc, splits,
+                                                 workspace.data_ptr(), ws_bytes, s)
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_splitk_ex")
     return C
@@ -358,9 +379,12 @@ def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, st
 def sgemm_splitk_atomic(A, B, C=None, alpha=1.0, beta=0.0, splits=0, stream=None):
     """Split-K with atomic accumulation into C (row-major operands; no
     workspace; not bitwise reproducible run to run)."""
+    import torch
     m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
-    st = lib.mi_sgemm_splitk_atomic(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
-                                    _stream(stream))
+    dev = _device_of(A, B, C)
+    with torch.cuda.device(dev):
+        st = lib.mi_sgemm_splitk_atomic(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
+                                        _stream(stream, dev))
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_splitk_atomic")
     return C
@@ -381,8 +405,10 @@ def reduce_sum(x, out=None, workspace=None, stream=None):
         workspace = torch.empty(max(mi_reduce_sum_workspace_bytes(n), 4), dtype=torch.uint8,
                                 device=x.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.mi_reduce_sum(n, x.data_ptr() if n else None, out.data_ptr(), workspace.data_ptr(),
-                           ws_bytes, _stream(stream))
+    dev = _device_of(x, out, workspace)
+    with torch.cuda.device(dev):
+        st = lib.mi_reduce_sum(n, x.data_ptr() if n else None, out.data_ptr(),
+                               workspace.data_ptr(), ws_bytes, _stream(stream, dev))
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_reduce_sum")
     return out

@@ -211,3 +211,15 @@ def test_reduce_sum_argument_errors_and_queries():
     d1 = hta.mi_reduce_sum_max_additions(1)
     dbig = hta.mi_reduce_sum_max_additions(1 << 28)
     assert 0 < d1 <= dbig < 400
+
+
+def test_helpers_refuse_mixed_devices():
+    """The torch helpers run each call with the operands' device current and
+    refuse operands on different devices (checked here with CPU and meta
+    tensors: the check comes before any device use)."""
+    import torch
+    a = torch.empty(2, 2)
+    b = torch.empty(2, 2, device="meta")
+    with pytest.raises(ValueError, match="different devices"):
+        hta._device_of(a, b)
+    assert hta._device_of(a, None, torch.empty(3)) == torch.device("cpu")
