@@ -21,8 +21,9 @@ __all__ = [
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
-    "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex",
-    "sgemm", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace", "reduce_sum",
+    "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex", "mi_sgemm_streamk",
+    "mi_sgemm_streamk_workspace_bytes",
+    "sgemm", "sgemm_streamk", "streamk_workspace", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace", "reduce_sum",
     "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "KERNEL_SPLITK_ATOMIC", "EXPORTED_SYMBOLS",
     "OP_N", "OP_T",
 ]
@@ -50,7 +51,8 @@ EXPORTED_SYMBOLS = (
     "mi_status_string", "mi_sgemm_get_plan", "mi_sgemm_config_count", "mi_sgemm_with_config",
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
-    "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex",
+    "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex", "mi_sgemm_streamk",
+    "mi_sgemm_streamk_workspace_bytes",
 )
 
 if not LIB_PATH.exists():
@@ -84,7 +86,7 @@ class Plan(ctypes.Structure):
         ("small_iterations", _i), ("fma_per_small_iteration", _i),
         ("outputs_per_thread", _i), ("a_elements_per_big_iteration", _i),
         ("b_elements_per_big_iteration", _i), ("group_m", _i), ("vector_loads", _i),
-        ("workspace_bytes", _sz),
+        ("workspace_bytes", _sz), ("stream_k_grid", _i),
     ]
 
     def as_dict(self):
@@ -109,6 +111,10 @@ lib.mi_sgemm_splitk_with_config.argtypes = [_i, _i, _i] + _GEMM_ARGS + [_i, _vp,
 lib.mi_sgemm_splitk_with_config.restype = _i
 lib.mi_sgemm_splitk_with_config_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.mi_sgemm_splitk_with_config_workspace_bytes.restype = _sz
+lib.mi_sgemm_streamk.argtypes = [_i, _i, _i] + _GEMM_ARGS + [_i, _vp, _sz, _vp]
+lib.mi_sgemm_streamk.restype = _i
+lib.mi_sgemm_streamk_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+lib.mi_sgemm_streamk_workspace_bytes.restype = _sz
 lib.mi_sgemm_splitk_atomic.argtypes = _GEMM_ARGS + [_i, _vp]
 lib.mi_sgemm_splitk_atomic.restype = _i
 lib.mi_reduce_sum.argtypes = [ctypes.c_longlong, _vp, _vp, _vp, _sz, _vp]
@@ -178,6 +184,16 @@ def mi_sgemm_splitk_with_config(config, trans_a, trans_b, m, n, k, alpha, A, lda
 
 def mi_sgemm_splitk_with_config_workspace_bytes(config, m, n, k, splits=0) -> int:
     return lib.mi_sgemm_splitk_with_config_workspace_bytes(config, m, n, k, splits)
+
+
+def mi_sgemm_streamk(config, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                     grid, ws, ws_bytes, stream=None) -> int:
+    return lib.mi_sgemm_streamk(config, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta,
+                                C, ldc, grid, ws, ws_bytes, stream)
+
+
+def mi_sgemm_streamk_workspace_bytes(config, m, n, k, grid=0) -> int:
+    return lib.mi_sgemm_streamk_workspace_bytes(config, m, n, k, grid)
 
 
 def mi_sgemm_splitk_atomic(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits=0,
@@ -373,6 +389,31 @@ def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, st
                                                  workspace.data_ptr(), ws_bytes, s)
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_splitk_ex")
+    return C
+
+
+def streamk_workspace(m, n, k, grid=0, device="cuda", config=-1):
+    """A device workspace tensor large enough for mi_sgemm_streamk."""
+    import torch
+    nbytes = mi_sgemm_streamk_workspace_bytes(config, m, n, k, grid)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def sgemm_streamk(A, B, C=None, alpha=1.0, beta=0.0, grid=0, workspace=None, stream=None,
+                  config=-1):
+    """Same as sgemm on a forced stream-K schedule (`grid` workgroups, 0 for
+    one per resident slot of every CU); `workspace` as streamk_workspace."""
+    import torch
+    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc = _prepare_ex(A, B, C, beta)
+    if workspace is None:
+        workspace = streamk_workspace(m, n, k, grid, device=A.device, config=config)
+    dev = _device_of(A, B, C, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib.mi_sgemm_streamk(config, ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc,
+                                  ldc, grid, workspace.data_ptr(), ws_bytes, _stream(stream, dev))
+    if st != SUCCESS:
+        raise MiSgemmError(st, "mi_sgemm_streamk")
     return C
 
 

@@ -11,7 +11,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Epilogue modes of the matrix-core kernel (see sgemm_mfma.hpp).
-constexpr int kFull = 0, kPartial = 1, kAtomic = 2;
+constexpr int kFull = 0, kPartial = 1, kAtomic = 2, kStreamK = 3;
 
 // MI355X places workgroups on its 8 XCDs (each with a private L2) round-robin
 // by workgroup id.
@@ -35,7 +35,21 @@ struct GemmArgs {
     float *ws;             // split-K: partials, slice s at ws + s * ws_slice
     long long ws_slice;    // split-K: floats per slice (>= m * n, multiple of 64)
     int c_vec;             // 1 when C is 16-byte aligned and ldc % 4 == 0
+    long long sk_iters;    // stream-K: (shared tiles) * k steps per tile
+    int sk_ksteps;         // stream-K: k steps per tile
+    int sk_dp_tiles;       // stream-K: leading tiles computed whole, one per workgroup
 };
+
+// Stream-K partition of `iters` (tile, k step) iterations over `grid`
+// workgroups: workgroup w takes [sk_begin(w), sk_begin(w + 1)), and the
+// iteration x belongs to workgroup sk_owner(x) (the last w whose range starts
+// at or before x).
+__host__ __device__ __forceinline__ long long sk_begin(long long w, long long iters, long long grid) {
+    return w * iters / grid;
+}
+__host__ __device__ __forceinline__ long long sk_owner(long long x, long long iters, long long grid) {
+    return ((x + 1) * grid + iters - 1) / iters - 1;
+}
 
 // Renumbers workgroups so that each XCD owns one contiguous range of logical
 // ids: hardware id w runs on XCD w % 8 as that XCD's (w / 8)-th workgroup.

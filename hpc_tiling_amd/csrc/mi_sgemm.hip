@@ -28,6 +28,8 @@ struct MfmaConfig {
     KernelFn full[2][2][2];   // full-k kernels
     KernelFn split[2][2][2];  // split-K partial kernels
     KernelFn atomic[2];       // split-K kernels adding into C atomically (operands as given)
+    KernelFn streamk[2][2][2];  // stream-K kernels
+    const void *fixup;          // stream-K fixup for this tile size
 };
 
 template <class T, int MODE, bool TA, bool TB>
@@ -46,10 +48,12 @@ constexpr void fill_table(KernelFn (&f)[2][2][2]) {
 
 template <class T>
 constexpr MfmaConfig make_cfg() {
-    MfmaConfig c{T::BM, T::BN, T::BK, T::WGM, T::WGN, {}, {}, {}};
+    MfmaConfig c{T::BM, T::BN, T::BK, T::WGM, T::WGN, {}, {}, {}, {}, nullptr};
     fill_table<T, kFull>(c.full);
     fill_table<T, kPartial>(c.split);
     fill_pair<T, kAtomic, false, false>(c.atomic);
+    fill_table<T, kStreamK>(c.streamk);
+    c.fixup = reinterpret_cast<const void *>(&streamk_fixup_kernel<T::BM, T::BN>);
     return c;
 }
 
@@ -123,6 +127,11 @@ struct SplitPlan {
     int k_per_split;   // multiple of the k step
     long long slice;   // floats per workspace slice
     size_t bytes;      // workspace bytes including alignment slack (0 for one slice)
+    int sk_grid;       // > 0: a stream-K schedule with this many workgroups instead
+    long long sk_iters;  // stream-K: shared tiles * k steps
+    int sk_ksteps;       // stream-K: k steps per tile
+    long long sk_dp_tiles;  // stream-K: leading tiles computed whole, one per workgroup
+    int sk_workers;         // stream-K: workgroups sharing the other tiles (0 or sk_grid)
 };
 
 constexpr size_t kWsAlign = 256;
@@ -130,7 +139,7 @@ constexpr size_t kWsAlign = 256;
 // Slices of k for a request of `want` (>= 1): whole k steps per slice; the
 // slice count that results may be smaller than asked.
 SplitPlan make_plan(int m, int n, int k, long long want, int config) {
-    SplitPlan sp{config, 0, 0, 0, 0};
+    SplitPlan sp{config, 0, 0, 0, 0, 0, 0, 0};
     if (m <= 0 || n <= 0 || k <= 0) return sp;
     const MfmaConfig &c = kMfmaConfigs[config];
     const long long kps = ceil_div(ceil_div(k, want), c.bk) * c.bk;
@@ -177,13 +186,80 @@ double config_efficiency(int id) {
     return 0.9;
 }
 
+// Workgroups of configuration `config` one CU holds at once (LDS and wave
+// slots).
+long long resident_per_cu(int config) {
+    const MfmaConfig &c = kMfmaConfigs[config];
+    const long long lds = 3LL * (c.bm * c.bk + c.bk * c.bn) * 4;
+    const long long waves = (long long)c.wgm * c.wgn;
+    long long r = (160LL * 1024) / lds;
+    if (r > 32 / waves) r = 32 / waves;
+    return r < 1 ? 1 : r;
+}
+
+// A stream-K schedule for `grid` workgroups' worth of concurrent work (0: one
+// per resident slot of every CU; never more than the iteration count or the
+// fixup's part limit).  When the tiles fill whole rounds of the grid, every
+// tile gets a workgroup of its own (no stream-K part).  Otherwise all rounds
+// but the last full one do (data-parallel tiles), and `grid` more workgroups
+// share the (tile, k step) iterations of the remaining tiles evenly (between
+// one and two rounds' worth of tiles, or all of them when there are fewer
+// than two rounds).  Workspace: two tile-sized slots per stream-K
+// workgroup.
+SplitPlan make_sk_plan(int m, int n, int k, int config, long long grid) {
+    SplitPlan sp{config, 1, k, 0, 0, 0, 0, 0, 0};
+    if (m <= 0 || n <= 0 || k <= 0) return sp;
+    const MfmaConfig &c = kMfmaConfigs[config];
+    const long long ksteps = ceil_div(k, c.bk);
+    const long long tiles = tile_count(m, n, config);
+    if (grid <= 0) grid = kCUs * resident_per_cu(config);
+    if (grid > tiles * ksteps) grid = tiles * ksteps;
+    if (grid > kFixupMaxParts) grid = kFixupMaxParts;
+    long long dp = 0;
+    if (tiles % grid == 0) dp = tiles;
+    else if (tiles >= 2 * grid) dp = (tiles / grid - 1) * grid;
+    sp.sk_grid = (int)grid;
+    sp.sk_workers = dp == tiles ? 0 : (int)grid;
+    sp.sk_dp_tiles = dp;
+    sp.sk_iters = (tiles - dp) * ksteps;
+    sp.sk_ksteps = (int)ksteps;
+    sp.bytes = sp.sk_workers > 0
+                   ? (size_t)sp.sk_workers * 2 * (size_t)c.bm * c.bn * sizeof(float) + kWsAlign
+                   : 0;
+    return sp;
+}
+
+// Modelled time (us) of a stream-K schedule: every workgroup runs its whole
+// tiles and ceil(shared iterations / grid) k steps (the CUs' resident
+// workgroups share the matrix cores), one prologue / epilogue per tile or
+// segment, and the fixup reads the parts of at most grid - 1 shared tiles
+// (about ksteps / share + 1 parts each).
+double sk_cost_us(int m, int n, const SplitPlan &sp, double efficiency) {
+    (void)m;
+    (void)n;
+    const MfmaConfig &c = kMfmaConfigs[sp.config];
+    const double step_us = 2.0 * c.bm * c.bn * c.bk / 256.0 / efficiency / kClockMHz;
+    const long long rounds = sp.sk_dp_tiles / sp.sk_grid;
+    const long long share = ceil_div(sp.sk_iters, sp.sk_grid);
+    const long long per_wg = rounds * sp.sk_ksteps + share;
+    const long long per_cu = ceil_div(sp.sk_grid, kCUs);
+    double t = (double)per_cu * per_wg * step_us;
+    if (share == 0) return t + (double)rounds * kWorkgroupOverheadUs;
+    const long long segments = rounds + ceil_div(share, sp.sk_ksteps) + 1;
+    long long shared = sp.sk_grid - 1;
+    if (shared > sp.sk_iters / sp.sk_ksteps) shared = sp.sk_iters / sp.sk_ksteps;
+    const double parts = (double)sp.sk_ksteps / (double)share + 1.0;
+    return t + (double)segments * kWorkgroupOverheadUs + kCombineFixedUs +
+           4.0 * c.bm * c.bn * (double)shared * parts / kCombineBytesPerUs;
+}
+
 // The split plan for a call: `splits` > 0 fixes the slice count (rounded to
 // whole k steps), 0 lets the model choose it; `config` >= 0 fixes the tile
 // configuration.  A plan of one slice runs the full-k kernel, and then (when
 // the configuration is free) with the tiles mi_sgemm would choose.  Measured
 // on MI355X at 512 x 512 x 262144: 16 slices of the 128 x 128 x 32 tile, one
 // round of 256 workgroups.
-SplitPlan plan_split(int m, int n, int k, int splits, int config) {
+SplitPlan plan_split(int m, int n, int k, int splits, int config, bool allow_sk = true) {
     if (m <= 0 || n <= 0 || k <= 0) return SplitPlan{config < 0 ? 0 : config, 0, 0, 0, 0};
     SplitPlan best{};
     double best_cost = 0.0;
@@ -208,9 +284,20 @@ SplitPlan plan_split(int m, int n, int k, int splits, int config) {
         const long long ksteps = ceil_div(k, kMfmaConfigs[id].bk);
         for (long long want = 1; want <= 256 && want <= ksteps; want += (want < 32 ? 1 : 4))
             consider(id, want);
+        // stream-K, when every workgroup's share spans at least a quarter of
+        // a tile's k steps (a shared tile then has at most about five parts)
+        const SplitPlan sk = make_sk_plan(m, n, k, id, 0);
+        if (allow_sk && 4 * (sk.sk_iters / sk.sk_grid) >= sk.sk_ksteps &&
+            sk.bytes <= kAutoWorkspaceCap) {
+            const double cost = sk_cost_us(m, n, sk, config_efficiency(id));
+            if (cost < best_cost * 0.97) {
+                best = sk;
+                best_cost = cost;
+            }
+        }
     }
     if (!have) best = make_plan(m, n, k, splits > 0 ? splits : 1, config);  // forced non-candidate
-    if (best.splits == 1 && config < 0) best.config = choose_mfma_config(m, n, k);
+    if (best.splits == 1 && best.sk_grid == 0 && config < 0) best.config = choose_mfma_config(m, n, k);
     return best;
 }
 
@@ -347,6 +434,31 @@ int run_valu(int config, int m, int n, int k, float alpha, const float *A, int l
     return launch(fn, grid, ValuTile::NT, s, a);
 }
 
+// Stream-K: the persistent-grid kernel, then the fixup of shared tiles.
+int launch_streamk(const SplitPlan &sp, int ta, int tb, int m, int n, int k, float alpha,
+                   const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                   int ldc, void *ws, hipStream_t s) {
+    float *wsa = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + kWsAlign - 1) &
+                                           ~(uintptr_t)(kWsAlign - 1));
+    const MfmaConfig &c = kMfmaConfigs[sp.config];
+    GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
+    a.tiles_m = (int)ceil_div(m, c.bm);
+    a.tiles_n = (int)ceil_div(n, c.bn);
+    a.ws = wsa;
+    a.sk_iters = sp.sk_iters;
+    a.sk_ksteps = sp.sk_ksteps;
+    a.sk_dp_tiles = (int)sp.sk_dp_tiles;
+    int st = launch(c.streamk[ta][tb][vector_ok(A, lda, B, ldb)], sp.sk_dp_tiles + sp.sk_workers,
+                    64 * c.wgm * c.wgn, s, a);
+    if (st || sp.sk_workers < 2) return st;
+    const float *wsc = wsa;
+    long long iters = sp.sk_iters, ldc64 = ldc;
+    int ksteps = sp.sk_ksteps, grid = sp.sk_workers, tile0 = a.sk_dp_tiles;
+    int tm = a.tiles_m, tn = a.tiles_n, gm = a.group_m;
+    void *args[] = {&wsc, &iters, &ksteps, &grid, &tile0, &tm, &tn, &gm, &m, &n, &alpha, &beta, &C, &ldc64};
+    return launch_raw(c.fixup, sp.sk_workers - 1, kFixupThreads, args, s);
+}
+
 int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, const float *A,
                int lda, const float *B, int ldb, float beta, float *C, int ldc, int splits,
                void *ws, size_t ws_bytes, void *stream) {
@@ -367,6 +479,7 @@ int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, con
     st = check_device();
     if (st) return st;
     const int id = sp.config;
+    if (sp.sk_grid > 0) return launch_streamk(sp, ta, tb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws, s);
     // one slice: the full-k kernel, no workspace (the same sums and rounding
     // as the partial-plus-combine path would give)
     if (sp.splits == 1) return launch_full(id, ta, tb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s);
@@ -408,7 +521,7 @@ int run_splitk_atomic(int config, int m, int n, int k, float alpha, const float 
     if (st) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (k == 0 || alpha == 0.f) return launch_scale(m, n, beta, C, ldc, s);
-    const SplitPlan sp = plan_split(m, n, k, splits, config);
+    const SplitPlan sp = plan_split(m, n, k, splits, config, false);  // slices only
     const int id = sp.config;
     if (sp.splits == 1) return launch_full(id, 0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s);
     if (beta != 1.f) {
@@ -422,6 +535,45 @@ int run_splitk_atomic(int config, int m, int n, int k, float alpha, const float 
     a.k_per_split = sp.k_per_split;
     const long long grid = (long long)a.tiles_m * a.tiles_n * sp.splits;
     return launch(c.atomic[vector_ok(A, lda, B, ldb)], grid, 64 * c.wgm * c.wgn, s, a);
+}
+
+// Stream-K with a forced grid (0: automatic) and configuration (< 0: the
+// candidate the model prefers).
+SplitPlan plan_streamk(int m, int n, int k, int config, int grid) {
+    if (config >= 0) return make_sk_plan(m, n, k, config, grid);
+    SplitPlan best{};
+    double best_cost = 0.0;
+    for (const Candidate &cand : kCandidates) {
+        const SplitPlan sp = make_sk_plan(m, n, k, cand.id, grid);
+        if (sp.sk_grid == 0) return sp;  // empty problem
+        const double cost = sk_cost_us(m, n, sp, cand.efficiency);
+        if (best.sk_grid == 0 || cost < best_cost * 0.99) {
+            best = sp;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+int run_streamk(int config, int ta, int tb, int m, int n, int k, float alpha, const float *A,
+                int lda, const float *B, int ldb, float beta, float *C, int ldc, int grid,
+                void *ws, size_t ws_bytes, void *stream) {
+    if (config >= kNumMfmaConfigs || grid < 0) return MI_SGEMM_ERROR_INVALID_VALUE;
+    int st = check_sizes(m, n, k, lda, ldb, ldc, ta, tb);
+    if (st) return st;
+    st = check_pointers(m, n, k, alpha, A, B, C);
+    if (st) return st;
+    if (m == 0 || n == 0) return MI_SGEMM_SUCCESS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k == 0 || alpha == 0.f) {
+        st = check_device();
+        return st ? st : launch_scale(m, n, beta, C, ldc, s);
+    }
+    const SplitPlan sp = plan_streamk(m, n, k, config, grid);
+    if (sp.bytes > 0 && (!ws || ws_bytes < sp.bytes)) return MI_SGEMM_ERROR_WORKSPACE;
+    st = check_device();
+    if (st) return st;
+    return launch_streamk(sp, ta, tb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -503,6 +655,18 @@ int mi_sgemm_splitk_atomic(int m, int n, int k, float alpha, const float *A, int
     return run_splitk_atomic(-1, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits, stream);
 }
 
+int mi_sgemm_streamk(int config, int trans_a, int trans_b, int m, int n, int k, float alpha,
+                     const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                     int ldc, int grid, void *ws, size_t ws_bytes, void *stream) {
+    return run_streamk(config, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                       grid, ws, ws_bytes, stream);
+}
+
+size_t mi_sgemm_streamk_workspace_bytes(int config, int m, int n, int k, int grid) {
+    if (m < 0 || n < 0 || k < 0 || grid < 0 || config >= kNumMfmaConfigs) return 0;
+    return plan_streamk(m, n, k, config, grid).bytes;
+}
+
 size_t mi_sgemm_splitk_with_config_workspace_bytes(int config, int m, int n, int k, int splits) {
     if (m < 0 || n < 0 || k < 0 || splits < 0 || splits > k || config >= kNumMfmaConfigs)
         return 0;
@@ -581,6 +745,7 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
     plan->vector_loads = 1;
     plan->splits = 1;
     plan->k_per_split = k;
+    long long sk_workgroups = 0;
     if (kernel == MI_SGEMM_KERNEL_VALU) {
         if (config > 0) return MI_SGEMM_ERROR_INVALID_VALUE;
         plan->config = 0;
@@ -598,7 +763,7 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
         if (split) {
             if (config >= kNumMfmaConfigs || splits < 0 || splits > k)
                 return MI_SGEMM_ERROR_INVALID_VALUE;
-            sp = plan_split(m, n, k, splits, config);
+            sp = plan_split(m, n, k, splits, config, kernel == MI_SGEMM_KERNEL_SPLITK);
             id = (m > 0 && n > 0 && k > 0) ? sp.config
                                            : (config < 0 ? choose_mfma_config(m, n, k) : config);
         } else {
@@ -614,6 +779,8 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
         plan->fma_per_small_iteration = (plan->micro_m / 32) * (plan->micro_n / 32);
         plan->outputs_per_thread = plan->micro_m * plan->micro_n / 64;
         if (split) {
+            plan->stream_k_grid = kernel == MI_SGEMM_KERNEL_SPLITK ? sp.sk_grid : 0;
+            if (plan->stream_k_grid > 0) sk_workgroups = sp.sk_dp_tiles + sp.sk_workers;
             plan->splits = sp.splits;
             plan->k_per_split = sp.k_per_split;
             plan->workspace_bytes = kernel == MI_SGEMM_KERNEL_SPLITK ? sp.bytes : 0;
@@ -623,7 +790,9 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
     }
     plan->tiles_m = (int)ceil_div(m, plan->tile_m);
     plan->tiles_n = (int)ceil_div(n, plan->tile_n);
-    plan->workgroups = (long long)plan->tiles_m * plan->tiles_n * (plan->splits > 0 ? plan->splits : 1);
+    plan->workgroups = sk_workgroups > 0
+                           ? sk_workgroups
+                           : (long long)plan->tiles_m * plan->tiles_n * (plan->splits > 0 ? plan->splits : 1);
     plan->big_iterations = (int)ceil_div(plan->k_per_split, plan->tile_k);
     plan->a_elements_per_big_iteration = plan->tile_m * plan->tile_k;
     plan->b_elements_per_big_iteration = plan->tile_k * plan->tile_n;

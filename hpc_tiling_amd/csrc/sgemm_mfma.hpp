@@ -79,6 +79,7 @@ struct Vals4 {
 // KROWS: the operand is e-contiguous, so LDS rows are k rows.
 template <class T, int E, bool KROWS>
 struct Operand {
+    static constexpr bool K_ROWS = KROWS;
     static constexpr int ROWS = KROWS ? T::BK : E;         // LDS tile rows
     static constexpr int CH = KROWS ? E / 4 : T::BK / 4;   // 16-byte chunks per row
     static constexpr int PER = ROWS * CH / T::NT;          // chunks per thread per step
@@ -158,13 +159,17 @@ struct Operand {
             sw = swz(e);
         }
     }
-    // The four values lane (l, h) feeds MFMAs s = 0..3 of group g: X[e][8g+4h+s].
-    __device__ static void frag_read(Frag &f, const float *buf, int off, int sw, int g, int lh) {
+    // The four values lane (l, h) feeds MFMAs s = 0..3 of group g: X[e][8g+4h+s],
+    // from word frag_addr(...) of the tile on.
+    __device__ static int frag_addr(int off, int sw, int g, int lh) {
+        return KROWS ? off + 8 * g * E : off + 4 * ((2 * g + lh) ^ sw);
+    }
+    __device__ static void frag_read(Frag &f, const float *buf, int addr) {
         if constexpr (KROWS) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) f[s] = buf[off + (8 * g + s) * E];
+            for (int s = 0; s < 4; ++s) f[s] = buf[addr + s * E];
         } else {
-            f = *reinterpret_cast<const f32x4 *>(buf + off + 4 * ((2 * g + lh) ^ sw));
+            f = *reinterpret_cast<const f32x4 *>(buf + addr);
         }
     }
 };
@@ -215,7 +220,7 @@ __device__ __forceinline__ void load_lds4(const float *base, float *lds, int vof
 // not wait for LDS at a step boundary.
 template <class T, bool VEC, int MODE, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
-    constexpr bool SPLIT = MODE != kFull;
+    constexpr bool SPLIT = MODE == kPartial || MODE == kAtomic;
     using OA = Operand<T, T::BM, TA>;    // A: k-contiguous unless given transposed
     using OB = Operand<T, T::BN, !TB>;   // B: n-contiguous unless given transposed
     // One LDS object per ring stage, always indexed at compile time: the
@@ -245,20 +250,10 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / T::WGN, wn = wave % T::WGN;
 
-    // ---- which tile (and slice) this workgroup computes -------------------
-    int id = xcd_contiguous(blockIdx.x, gridDim.x);
-    int slice = 0;
-    if (SPLIT) {
-        const int tiles = p.tiles_m * p.tiles_n;
-        slice = id / tiles;
-        id -= slice * tiles;
-    }
-    int tm, tn;
-    grouped_tile(id, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    const int m0 = tm * T::BM, n0 = tn * T::BN;
-    const int kbeg = SPLIT ? slice * p.k_per_split : 0;
-    const int kend = SPLIT ? min(p.k, kbeg + p.k_per_split) : p.k;
-    const int nsteps = (kend - kbeg + T::BK - 1) / T::BK;
+    // ---- the tile (and k range) being computed ------------------------------
+    // Set once per workgroup, or once per segment of its stream-K range.
+    int m0 = 0, n0 = 0, kbeg = 0, kend = 0, nsteps = 0, ndirect = 0, a_lim = 0, b_lim = 0;
+    const float *Ablk = p.A, *Bblk = p.B;
     // Whole k steps are loaded directly into LDS (byte offsets inside one
     // tile step must fit the 31-bit buffer offset): 16 bytes per lane for
     // aligned operands, 4 bytes otherwise.  On the m / n edge, rows, chunks
@@ -266,11 +261,22 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     // feed outputs that are never stored, and every address stays inside the
     // operands.
     const bool direct_ok = OA::direct_fits(p.lda) && OB::direct_fits(p.ldb);
-    const int ndirect = direct_ok ? (kend - kbeg) / T::BK : 0;
-    const int a_lim = VEC ? OA::clamp_limit(min(T::BM, p.m - m0)) : min(T::BM, p.m - m0) - 1;
-    const int b_lim = VEC ? OB::clamp_limit(min(T::BN, p.n - n0)) : min(T::BN, p.n - n0) - 1;
-    const float *Ablk = OA::block_base(p.A, p.lda, m0);
-    const float *Bblk = OB::block_base(p.B, p.ldb, n0);
+    auto set_tile = [&](int tile, int kb, int ke) {
+        int tm, tn;
+        grouped_tile(tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+        m0 = tm * T::BM;
+        n0 = tn * T::BN;
+        kbeg = kb;
+        kend = ke;
+        nsteps = (kend - kbeg + T::BK - 1) / T::BK;
+        ndirect = direct_ok ? (kend - kbeg) / T::BK : 0;
+        a_lim = VEC ? OA::clamp_limit(min(T::BM, p.m - m0)) : min(T::BM, p.m - m0) - 1;
+        b_lim = VEC ? OB::clamp_limit(min(T::BN, p.n - n0)) : min(T::BN, p.n - n0) - 1;
+        // (the k offset is folded in here so that a step's base below is the
+        // same expression in every mode)
+        Ablk = OA::tile_base(OA::block_base(p.A, p.lda, m0), p.lda, kbeg);
+        Bblk = OB::tile_base(OB::block_base(p.B, p.ldb, n0), p.ldb, kbeg);
+    };
 
     // ---- direct global -> LDS loads (complete, aligned tiles) ---------------
     // buffer_load_dwordx4 ... lds through a per-step buffer resource whose
@@ -280,9 +286,8 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     // outstanding LDS read before each MFMA group.)
     auto load_direct = [&](int step, auto buf) {
         float *as = a_buf(buf), *bs = b_buf(buf);
-        const int k0 = kbeg + step * T::BK;
-        const float *abase = OA::tile_base(Ablk, p.lda, k0);
-        const float *bbase = OB::tile_base(Bblk, p.ldb, k0);
+        const float *abase = OA::tile_base(Ablk, p.lda, step * T::BK);
+        const float *bbase = OB::tile_base(Bblk, p.ldb, step * T::BK);
         if constexpr (VEC) {
 #pragma unroll
             for (int i = 0; i < OA::PER; ++i) {
@@ -342,12 +347,14 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
 
     // ---- accumulators and fragments ----------------------------------------
     f32x16 acc[T::FM][T::FN];
+    auto clear_acc = [&]() {
 #pragma unroll
-    for (int a = 0; a < T::FM; ++a)
+        for (int a = 0; a < T::FM; ++a)
 #pragma unroll
-        for (int b = 0; b < T::FN; ++b)
+            for (int b = 0; b < T::FN; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+                for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    };
 
     const int li = lane & 31, lh = lane >> 5;
     int a_off[T::FM], a_sw[T::FM], b_off[T::FN], b_sw[T::FN];
@@ -360,12 +367,33 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
         typename OA::Frag a[T::FM];
         typename OB::Frag b[T::FN];
     };
+    // Word offsets of every group's fragment reads.  Set at the start of each
+    // run of k steps: (for an operand whose reads are swizzled per group)
+    // they then live only through the loop, which keeps a persistent
+    // workgroup's compiler from rebuilding them inside the loop to free
+    // registers for the epilogue.
+    int a_addr[T::FM][T::GROUPS], b_addr[T::FN][T::GROUPS];
+    auto set_frag_addr = [&]() {
+#pragma unroll
+        for (int g = 0; g < T::GROUPS; ++g) {
+#pragma unroll
+            for (int a = 0; a < T::FM; ++a) {
+                a_addr[a][g] = OA::frag_addr(a_off[a], a_sw[a], g, lh);
+                if constexpr (MODE == kStreamK && !OA::K_ROWS) asm volatile("" : "+v"(a_addr[a][g]));
+            }
+#pragma unroll
+            for (int b = 0; b < T::FN; ++b) {
+                b_addr[b][g] = OB::frag_addr(b_off[b], b_sw[b], g, lh);
+                if constexpr (MODE == kStreamK && !OB::K_ROWS) asm volatile("" : "+v"(b_addr[b][g]));
+            }
+        }
+    };
     auto read_frag = [&](Frag &f, auto buf, int g) {
         const float *as = a_buf(buf), *bs = b_buf(buf);
 #pragma unroll
-        for (int a = 0; a < T::FM; ++a) OA::frag_read(f.a[a], as, a_off[a], a_sw[a], g, lh);
+        for (int a = 0; a < T::FM; ++a) OA::frag_read(f.a[a], as, a_addr[a][g]);
 #pragma unroll
-        for (int b = 0; b < T::FN; ++b) OB::frag_read(f.b[b], bs, b_off[b], b_sw[b], g, lh);
+        for (int b = 0; b < T::FN; ++b) OB::frag_read(f.b[b], bs, b_addr[b][g]);
     };
     auto mfma_group = [&](const Frag &f) {
 #pragma unroll
@@ -381,7 +409,9 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     // ---- main loop -----------------------------------------------------------
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
+    auto run_steps = [&]() {
     if (nsteps > 0) {
+        set_frag_addr();
         Frag f[2];
         // make the tiles of steps 0 and 1 resident
         auto fill = [&](int step, auto buf) {
@@ -451,34 +481,102 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
         for (; step + 2 < ndirect; ++step) dispatch(step, std::true_type{});
         for (; step < nsteps; ++step) dispatch(step, std::false_type{});
     }
+    };
 
     // ---- epilogue -----------------------------------------------------------
     // Accumulator register r of lane (j, h) holds C row 8*(r/4) + 4*h + r%4,
-    // column j of its 32x32 block.
+    // column j of its 32x32 block.  `store(row, col, v)` gets every in-range
+    // element of the tile.
+    auto for_each_output = [&](auto store) {
 #pragma unroll
-    for (int a = 0; a < T::FM; ++a) {
+        for (int a = 0; a < T::FM; ++a) {
 #pragma unroll
-        for (int b = 0; b < T::FN; ++b) {
-            const int col = n0 + wn * T::WTN + 32 * b + li;
+            for (int b = 0; b < T::FN; ++b) {
+                const int col = n0 + wn * T::WTN + 32 * b + li;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * T::WTM + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (row < p.m && col < p.n) {
-                    if constexpr (MODE == kPartial) {
-                        p.ws[(long long)slice * p.ws_slice + (long long)row * p.n + col] = acc[a][b][r];
-                    } else if constexpr (MODE == kAtomic) {
-                        unsafeAtomicAdd(p.C + (long long)row * p.ldc + col, p.alpha * acc[a][b][r]);
-                    } else {
-                        // C is touched once: nontemporal access (measured
-                        // about 1 % faster at 2048^3 and 8192^3, probably
-                        // less dirty L2 to write back when the kernel ends).
-                        float *dst = p.C + (long long)row * p.ldc + col;
-                        float v = p.alpha * acc[a][b][r];
-                        if (p.beta != 0.f) v = __builtin_fmaf(p.beta, __builtin_nontemporal_load(dst), v);
-                        __builtin_nontemporal_store(v, dst);
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * T::WTM + 32 * a + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    if (row < p.m && col < p.n) store(row, col, acc[a][b][r]);
                 }
             }
+        }
+    };
+    // C = alpha * acc + beta * C.  C is touched once: nontemporal access
+    // (measured about 1 % faster at 2048^3 and 8192^3, probably less dirty L2
+    // to write back when the kernel ends).
+    auto store_c = [&]() {
+        for_each_output([&](int row, int col, float v) {
+            float *dst = p.C + (long long)row * p.ldc + col;
+            float r = p.alpha * v;
+            if (p.beta != 0.f) r = __builtin_fmaf(p.beta, __builtin_nontemporal_load(dst), r);
+            __builtin_nontemporal_store(r, dst);
+        });
+    };
+
+    if constexpr (MODE == kStreamK) {
+        // Data-parallel tiles, then stream-K.  The first sk_dp_tiles
+        // workgroups each compute one whole tile, in the order of the
+        // one-tile-per-workgroup launch (the hardware hands them to CUs as
+        // CUs free up, which balances the load); the remaining `grid` share
+        // the (tile, k step) iterations of the tiles after those evenly, one
+        // segment per tile a workgroup's range touches.  A segment that
+        // covers its tile's whole k range is finished here; the others leave
+        // their raw sums in the workgroup's slot 0 (a segment that starts
+        // inside its tile) or slot 1 (one that starts at the tile's first step
+        // and stops inside it), for the fixup kernel.  A workgroup has at most
+        // one segment of each kind.
+        const int h = blockIdx.x;
+        const int dp = p.sk_dp_tiles;
+        long long w = -1, it, end, tile0 = 0;
+        if (h < dp) {
+            it = (long long)xcd_contiguous(h, dp) * p.sk_ksteps;
+            end = it + p.sk_ksteps;
+        } else {
+            const long long grid = gridDim.x - dp;
+            w = xcd_contiguous(h - dp, (int)grid);
+            it = sk_begin(w, p.sk_iters, grid);
+            end = sk_begin(w + 1, p.sk_iters, grid);
+            tile0 = dp;
+        }
+        while (it < end) {
+            const long long t = it / p.sk_ksteps;
+            const int ks = (int)(it - t * p.sk_ksteps);
+            const int ke = (int)min((long long)p.sk_ksteps, ks + (end - it));
+            set_tile((int)(tile0 + t), ks * T::BK, min(p.k, ke * T::BK));
+            clear_acc();
+            run_steps();
+            if (ks == 0 && ke == p.sk_ksteps) {
+                store_c();
+            } else {
+                float *slot = p.ws + (w * 2 + (ks > 0 ? 0 : 1)) * (long long)(T::BM * T::BN);
+                for_each_output([&](int row, int col, float v) {
+                    slot[(row - m0) * T::BN + (col - n0)] = v;
+                });
+            }
+            it += ke - ks;
+        }
+    } else {
+        int id = xcd_contiguous(blockIdx.x, gridDim.x);
+        int slice = 0;
+        if (SPLIT) {
+            const int tiles = p.tiles_m * p.tiles_n;
+            slice = id / tiles;
+            id -= slice * tiles;
+        }
+        const int kb = SPLIT ? slice * p.k_per_split : 0;
+        set_tile(id, kb, SPLIT ? min(p.k, kb + p.k_per_split) : p.k);
+        clear_acc();
+        run_steps();
+        if constexpr (MODE == kPartial) {
+            for_each_output([&](int row, int col, float v) {
+                p.ws[(long long)slice * p.ws_slice + (long long)row * p.n + col] = v;
+            });
+        } else if constexpr (MODE == kAtomic) {
+            for_each_output([&](int row, int col, float v) {
+                unsafeAtomicAdd(p.C + (long long)row * p.ldc + col, p.alpha * v);
+            });
+        } else {
+            store_c();
         }
     }
 }

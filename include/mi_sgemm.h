@@ -229,7 +229,8 @@ typedef struct mi_sgemm_plan {
     int micro_m, micro_n;  /* VALU: r_m, r_n per thread; MFMA: per-wave tile */
     int threads;           /* threads per workgroup */
     int tiles_m, tiles_n;  /* M = ceil(m / b_m), N = ceil(n / b_n) */
-    long long workgroups;  /* grid size of the main kernel */
+    long long workgroups;  /* grid size of the main kernel (stream-K: the
+                              data-parallel tiles plus the stream-K workgroups) */
     int splits;            /* K slices (1 when not split) */
     int k_per_split;       /* length of every slice but possibly the last */
     int big_iterations;    /* b_k steps per workgroup: ceil(k_per_split / b_k) */
@@ -242,6 +243,10 @@ typedef struct mi_sgemm_plan {
     int group_m;           /* height, in tiles, of the grouped workgroup order */
     int vector_loads;      /* 1 when 16-byte loads of A and B are used */
     size_t workspace_bytes;
+    int stream_k_grid;     /* > 0: the split-K entry runs a stream-K schedule for
+                              this many concurrent workgroups (see
+                              mi_sgemm_streamk; splits then 1, big_iterations
+                              the tile's k steps) */
 } mi_sgemm_plan;
 
 /*
@@ -287,6 +292,34 @@ int mi_sgemm_splitk_with_config(int config, int trans_a, int trans_b,
                                 int splits, void *ws, size_t ws_bytes, void *stream);
 size_t mi_sgemm_splitk_with_config_workspace_bytes(int config, int m, int n, int k,
                                                    int splits);
+
+/*
+ * mi_sgemm_streamk -- the product on a stream-K schedule, for shapes whose
+ * tiles leave the last round of workgroups partly empty.  With G = grid
+ * (0: one per resident workgroup slot of every CU; capped by the number of
+ * (tile, k step) iterations and by 2048): when the tile count is a multiple
+ * of G every tile gets a workgroup of its own, as in mi_sgemm.  Otherwise
+ * all rounds of G tiles but the last full one do (data-parallel tiles), and
+ * G more workgroups each take an equal share of the (tile, k step)
+ * iterations of the remaining tiles (between one and two rounds' worth, or
+ * all tiles when there are fewer than two rounds).  Such a workgroup
+ * finishes the tiles whose whole k range falls in its share, leaves the raw
+ * sums of the tiles cut at the ends of its share in its two workspace slots,
+ * and a second kernel adds the parts of every cut tile in a fixed order --
+ * deterministic, like mi_sgemm_splitk.  It is the big iteration over K of
+ * page "GEMM优化原理" (section 基于 shared memory 计算) divided by work
+ * rather than by tile.  mi_sgemm_splitk's automatic plan uses it when its
+ * model prefers it; this entry forces it.  config: tile configuration (ids
+ * as for MI_SGEMM_KERNEL_MFMA, < 0: the model's choice).  ws / ws_bytes: at
+ * least mi_sgemm_streamk_workspace_bytes(config, m, n, k, grid) bytes, two
+ * tiles per stream-K workgroup (0 for invalid arguments or when no tile is
+ * shared; ws may then be NULL).  Other arguments, semantics and errors as
+ * mi_sgemm_splitk_ex.
+ */
+int mi_sgemm_streamk(int config, int trans_a, int trans_b, int m, int n, int k, float alpha,
+                     const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                     int ldc, int grid, void *ws, size_t ws_bytes, void *stream);
+size_t mi_sgemm_streamk_workspace_bytes(int config, int m, int n, int k, int grid);
 
 #ifdef __cplusplus
 }

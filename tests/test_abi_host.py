@@ -223,3 +223,31 @@ def test_helpers_refuse_mixed_devices():
     with pytest.raises(ValueError, match="different devices"):
         hta._device_of(a, b)
     assert hta._device_of(a, None, torch.empty(3)) == torch.device("cpu")
+
+
+def test_streamk_argument_errors_and_plan():
+    E, f = hta, hta.mi_sgemm_streamk
+    ws = hta.mi_sgemm_streamk_workspace_bytes(-1, 100, 100, 100, 0)
+    assert ws > 0
+    assert f(-1, 0, 0, 100, 100, 100, 1.0, P, 100, P, 100, 0.0, P, 100, -1, P, ws) == E.ERROR_INVALID_VALUE
+    assert f(99, 0, 0, 100, 100, 100, 1.0, P, 100, P, 100, 0.0, P, 100, 0, P, ws) == E.ERROR_INVALID_VALUE
+    assert f(-1, 0, 0, 100, 100, 100, 1.0, P, 99, P, 100, 0.0, P, 100, 0, P, ws) == E.ERROR_INVALID_LD
+    assert f(-1, 0, 0, 100, 100, 100, 1.0, P, 100, P, 100, 0.0, P, 100, 0, P, ws - 1) == E.ERROR_WORKSPACE
+    assert f(-1, 0, 0, 100, 100, 100, 1.0, P, 100, P, 100, 0.0, P, 100, 0, None, ws) == E.ERROR_WORKSPACE
+    assert f(-1, 0, 0, 0, 100, 100, 1.0, None, 100, None, 100, 0.0, None, 100, 0, None, 0) == E.SUCCESS
+    assert hta.mi_sgemm_streamk_workspace_bytes(-1, 100, 100, 100, -1) == 0
+    # the grid never exceeds the number of (tile, k step) iterations; a grid
+    # that divides the tiles shares none (no workspace)
+    assert hta.mi_sgemm_streamk_workspace_bytes(6, 1, 1, 5, 1000) == 0
+    assert hta.mi_sgemm_streamk_workspace_bytes(6, 128, 128, 64, 4) == 0
+    # 4 tiles of 64 x 64, 3 workgroups: every tile's iterations are shared
+    assert hta.mi_sgemm_streamk_workspace_bytes(6, 100, 100, 100, 3) == 3 * 2 * 64 * 64 * 4 + 256
+    # 16 tiles, 3 workgroups: 12 whole tiles, the last 4 shared
+    assert hta.mi_sgemm_streamk_workspace_bytes(6, 256, 256, 100, 3) == 3 * 2 * 64 * 64 * 4 + 256
+    # the automatic split plan picks stream-K where its model prefers it
+    p = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, 1536, 1536, 4096, 0)
+    assert p["stream_k_grid"] > 0 and p["workgroups"] >= p["stream_k_grid"]
+    q = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, 512, 512, 262144, 0)
+    assert q["stream_k_grid"] == 0 and q["splits"] == 16
+    a = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK_ATOMIC, -1, 1536, 1536, 4096, 0)
+    assert a["stream_k_grid"] == 0

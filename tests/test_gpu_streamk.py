@@ -1,0 +1,126 @@
+"""GPU parity of the stream-K schedule (mi_sgemm_streamk, and mi_sgemm_splitk
+when its plan chooses it) against the CPU oracle.
+
+Grids are forced across the interesting regimes: one workgroup's worth
+(every tile whole, no fixup), grids that divide the tiles (likewise), fewer
+workgroups than tiles (whole-tile workgroups first, then the last one to two
+rounds' worth of tiles shared), about as many as tiles, and more than tiles
+(tiles shared by three or more workgroups); every tile configuration,
+transposes, k tails, beta != 0.  Integer-valued operands must be bit-exact; float operands within
+the tolerance of tests/parity.py; the schedule is deterministic.
+"""
+import numpy as np
+import pytest
+
+import synth
+from parity import assert_close, assert_exact
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import hpc_tiling_amd as hta
+    N_CFG = hta.mi_sgemm_config_count(hta.KERNEL_MFMA)
+else:
+    hta = None
+    N_CFG = 10
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_sk(w, ta, tb, integer, grid, config, orc):
+    A, lda, B, ldb, C = synth.operands_ex(w, ta, tb, integer_twin=integer)
+    say("streamk", w.name, w.m, w.n, w.k, ta, tb, "int" if integer else "float", "grid", grid, "cfg", config)
+    Ad = torch.from_numpy(A).cuda()
+    Bd = torch.from_numpy(B).cuda()
+    Cd = torch.from_numpy(C).cuda()
+    Av = Ad[:, :w.m].t() if ta else Ad[:, :w.k]
+    Bv = Bd[:, :w.k].t() if tb else Bd[:, :w.n]
+    hta.sgemm_streamk(Av, Bv, Cd[:, :w.n], w.alpha, w.beta, grid=grid, config=config)
+    torch.cuda.synchronize()
+    out = Cd.cpu().numpy()
+    assert np.array_equal(out[:, w.n:], C[:, w.n:]), "C padding written"
+    ref = orc.sgemm(w.m, w.n, w.k, w.alpha, A, lda, B, ldb, w.beta, C, w.ldc, want_g=True,
+                    trans_a=bool(ta), trans_b=bool(tb))
+    want = ref["C"].reshape(w.m, w.ldc)[:, :w.n]
+    what = f"streamk {w.m}x{w.n}x{w.k} ta={ta} tb={tb} grid={grid} cfg={config}"
+    if integer:
+        assert_exact(out[:, :w.n], want, what)
+    else:
+        assert_close(out[:, :w.n], want, ref["G"], w.alpha, w.beta, C[:, :w.n], what)
+    return out
+
+
+SHAPES = [(130, 257, 300), (255, 129, 1000), (64, 64, 2049), (300, 200, 33), (1, 1, 5)]
+GRIDS = [1, 2, 5, 37, 0, 300]
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
+def test_streamk_grids(orc, shape, grid):
+    m, n, k = shape
+    w = synth.Workload(6, "sk", m, n, k, k + 4, n + 4, n + 3, "uniform", "int3", 1.5, 0.5)
+    run_sk(w, 0, 0, True, grid, 6, orc)
+    run_sk(w.scaled(dist_c="uniform", alpha=1.0, beta=0.0), 0, 0, False, grid, 9, orc)
+
+
+@pytest.mark.parametrize("config", range(N_CFG))
+def test_streamk_every_config(orc, config):
+    w = synth.Workload(7, "skcfg", 333, 444, 555, 556, 448, 447, "uniform", "int3", 1.0, -1.0)
+    run_sk(w, 0, 0, True, 17, config, orc)
+    run_sk(w, 1, 1, True, 0, config, orc)
+
+
+# 1000 x 1000 has 256 tiles of 64 x 64 and 64 of 128 x 128: grids below half
+# the tile count run whole-tile rounds first and share only the last one to
+# two rounds' worth of tiles; grid 64 (128 x 128) and 128 (64 x 64) divide
+# the tiles and run whole tiles only.
+ROUND_CASES = [(6, 37), (6, 100), (6, 128), (9, 7), (9, 29), (9, 64)]
+
+
+@pytest.mark.parametrize("case", ROUND_CASES, ids=[f"cfg{c}-grid{g}" for c, g in ROUND_CASES])
+def test_streamk_whole_tile_rounds(orc, case):
+    config, grid = case
+    w = synth.Workload(8, "skrounds", 1000, 1000, 300, 304, 1001, 1002, "uniform", "int3", 1.0, 0.5)
+    run_sk(w, 0, 0, True, grid, config, orc)
+    run_sk(w, 1, 0, True, grid, config, orc)
+
+
+@pytest.mark.parametrize("combo", [(0, 1), (1, 0), (1, 1)], ids=["NT", "TN", "TT"])
+def test_streamk_transposed_and_unaligned(orc, combo):
+    ta, tb = combo
+    w = synth.Workload(8, "skt", 517, 389, 777, 779, 391, 390, "normal", "normal", 0.75, 2.0)
+    run_sk(w, ta, tb, False, 0, -1, orc)
+    run_sk(w, ta, tb, True, 23, 0, orc)
+
+
+def test_streamk_deterministic_and_auto_plan(orc):
+    """The automatic split plan takes stream-K at 1536 x 1536 x 4096; two
+    runs give the same bits, within the tolerance of the oracle."""
+    m = n = 1536
+    k = 4096
+    plan = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, m, n, k, 0)
+    say("streamk auto plan", plan["config"], plan["stream_k_grid"])
+    assert plan["stream_k_grid"] > 0
+    w = synth.Workload(9, "skauto", m, n, k, k, n, n, "uniform", None, 1.0, 0.0)
+    A, B, C = synth.operands(w)
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C1 = torch.empty((m, n), device="cuda")
+    C2 = torch.empty((m, n), device="cuda")
+    ws = hta.splitk_workspace(m, n, k, 0)
+    hta.sgemm_splitk(Ad, Bd, C1, splits=0, workspace=ws)
+    hta.sgemm_splitk(Ad, Bd, C2, splits=0, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    rows = synth.sample_rows([9, 1], m, 24)
+    ref = orc.sgemm(m, n, k, 1.0, A, k, B, n, 0.0, C, n, rows=rows, want_g=True)
+    assert_close(C1.cpu().numpy()[rows], ref["C"].reshape(m, n)[rows], ref["G"], 1.0, 0.0, 0.0,
+                 "auto stream-K")
