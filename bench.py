@@ -336,7 +336,8 @@ def main(argv=None):
                  ("mfma", "sgemm_256x256x256"),
                  ("mfma_nt", "sgemm_2048x2048x2048"), ("mfma_tn", "sgemm_2048x2048x2048"),
                  ("mfma_tt", "sgemm_2048x2048x2048"), ("mfma_tt", "sgemm_8192x8192x8192_ab"),
-                 ("splitk_tn", "sgemm_splitk_512x512x262144")]
+                 ("splitk_tn", "sgemm_splitk_512x512x262144"),
+                 ("mfma", "sgemm_1536x1536x4096"), ("splitk", "sgemm_1536x1536x4096")]
         line["secondary"] = secondary(pairs)
         line["secondary"].append(reduce_secondary())
 

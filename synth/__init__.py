@@ -67,6 +67,10 @@ WORKLOADS = [
              "uniform", None, 1.0, 0.0),
     Workload(4, "sgemm_splitk_512x512x262144", 512, 512, 262144, 262144, 512, 512,
              "uniform", None, 1.0, 0.0, splitk=True),
+    # an under-filled grid (144 tiles of 128 x 128 on 256 CUs): the split-K
+    # entry's plan runs it on the stream-K schedule
+    Workload(5, "sgemm_1536x1536x4096", 1536, 1536, 4096, 4096, 1536, 1536,
+             "uniform", None, 1.0, 0.0),
 ]
 
 
