@@ -456,7 +456,7 @@ int launch_streamk(const SplitPlan &sp, int ta, int tb, int m, int n, int k, flo
     int ksteps = sp.sk_ksteps, grid = sp.sk_workers, tile0 = a.sk_dp_tiles;
     int tm = a.tiles_m, tn = a.tiles_n, gm = a.group_m;
     void *args[] = {&wsc, &iters, &ksteps, &grid, &tile0, &tm, &tn, &gm, &m, &n, &alpha, &beta, &C, &ldc64};
-    return launch_raw(c.fixup, sp.sk_workers - 1, kFixupThreads, args, s);
+    return launch_raw(c.fixup, (long long)(sp.sk_workers - 1) * kFixupSplit, kFixupThreads, args, s);
 }
 
 int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, const float *A,

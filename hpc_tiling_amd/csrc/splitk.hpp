@@ -68,23 +68,25 @@ __global__ __launch_bounds__(256) void splitk_combine_kernel(const float *__rest
 }
 
 // Stream-K fixup over the shared tiles tile0, tile0 + 1, ... (`iters` is
-// their count times `ksteps`).  Block b (b = 1 .. grid - 1) looks at the
+// their count times `ksteps`).  Blocks come in groups of kFixupSplit, one per
+// band of rows of a tile.  Group b - 1 (b = 1 .. grid - 1) looks at the
 // iteration where workgroup b's range starts; if that is inside a tile, and b
-// is the first workgroup starting inside it, the tile was shared: its parts sit in the
-// slots of workgroups first .. last (the owners of the tile's first and last
-// iterations), and the block adds them in that order -- which is also k
-// order, so the result is fixed -- then writes C = alpha * sum + beta * C.
-// At most kFixupMaxParts workgroups may share one tile (the host keeps the
-// grid below that).
+// is the first workgroup starting inside it, the tile was shared: its parts
+// sit in the slots of workgroups first .. last (the owners of the tile's first
+// and last iterations), and the group adds them in that order -- which is
+// also k order, so the result is fixed -- then writes C = alpha * sum +
+// beta * C.  At most kFixupMaxParts workgroups may share one tile (the host
+// keeps the grid below that).
 constexpr int kFixupMaxParts = 2048;
-
-constexpr int kFixupThreads = 1024;
+constexpr int kFixupSplit = 4;
+constexpr int kFixupThreads = 256;
 
 template <int BM, int BN>
 __global__ __launch_bounds__(kFixupThreads) void streamk_fixup_kernel(
     const float *__restrict__ ws, long long iters, int ksteps, int grid, int tile0, int tiles_m,
     int tiles_n, int group_m, int m, int n, float alpha, float beta, float *C, long long ldc) {
-    const long long b = (long long)blockIdx.x + 1;
+    const long long b = (long long)(blockIdx.x / kFixupSplit) + 1;
+    const int band = blockIdx.x % kFixupSplit;
     const long long x = sk_begin(b, iters, grid);
     if (x >= iters || x % ksteps == 0) return;
     const long long t = x / ksteps;
@@ -104,28 +106,47 @@ __global__ __launch_bounds__(kFixupThreads) void streamk_fixup_kernel(
     }
     __syncthreads();
 
-    // Lane l holds the float4 groups l, l + 1024, ... of the tile (row-major,
-    // BN a multiple of 4); the parts are added in order, all of a part's
-    // loads in flight together.  Entries of the slots outside C's extent were
-    // never written and are not stored.
-    constexpr int PER = BM * BN / 4 / kFixupThreads;
-    static_assert(PER >= 1 && BM * BN % (4 * kFixupThreads) == 0, "tile must fill the block");
+    // Lane l of band j holds float4 groups j * BAND + l, j * BAND + l + 256,
+    // ... of the tile (row-major, BN a multiple of 4).  The parts are added in
+    // order, two parts' loads in flight together.  Entries of the slots
+    // outside C's extent were never written and are not stored.
+    constexpr int BAND = BM * BN / 4 / kFixupSplit;
+    constexpr int PER = BAND / kFixupThreads;
+    static_assert(PER >= 1 && BAND % kFixupThreads == 0, "a band must fill the block");
+    const int g0 = band * BAND + threadIdx.x;
+    auto part = [&](long long off, int u) -> f32x4 {
+        if (off < 0) return f32x4{0.f, 0.f, 0.f, 0.f};
+        return reinterpret_cast<const f32x4 *>(ws + off)[g0 + u * kFixupThreads];
+    };
     f32x4 acc[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < parts; ++q) {
-        const long long off = part_off[q];
-        if (off < 0) continue;
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(ws + off);
+    int q = 0;
+    for (; q + 1 < parts; q += 2) {
+        const long long o0 = part_off[q], o1 = part_off[q + 1];
+        f32x4 v0[PER], v1[PER];
 #pragma unroll
-        for (int u = 0; u < PER; ++u) acc[u] += src[threadIdx.x + u * kFixupThreads];
+        for (int u = 0; u < PER; ++u) {
+            v0[u] = part(o0, u);
+            v1[u] = part(o1, u);
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            acc[u] += v0[u];
+            acc[u] += v1[u];
+        }
+    }
+    if (q < parts) {
+        const long long o0 = part_off[q];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) acc[u] += part(o0, u);
     }
     int tm, tn;
     grouped_tile(tile0 + (int)t, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int e = 4 * (threadIdx.x + u * kFixupThreads);
+        const int e = 4 * (g0 + u * kFixupThreads);
         const int row = m0 + e / BN, col = n0 + e % BN;
         if (row >= m) continue;
 #pragma unroll
