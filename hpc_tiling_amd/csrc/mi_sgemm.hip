@@ -25,6 +25,8 @@ using KernelFn = void (*)(GemmArgs);
 // Kernel tables are indexed [trans_a][trans_b][vector loads].
 struct MfmaConfig {
     int bm, bn, bk, wgm, wgn;
+    int stages;    // LDS buffers in the ring
+    int max_wgs;   // workgroups per CU the register budget allows (0: no limit beyond LDS and waves)
     KernelFn full[2][2][2];   // full-k kernels
     KernelFn split[2][2][2];  // split-K partial kernels
     KernelFn atomic[2];       // split-K kernels adding into C atomically (operands as given)
@@ -48,7 +50,8 @@ constexpr void fill_table(KernelFn (&f)[2][2][2]) {
 
 template <class T>
 constexpr MfmaConfig make_cfg() {
-    MfmaConfig c{T::BM, T::BN, T::BK, T::WGM, T::WGN, {}, {}, {}, {}, nullptr};
+    MfmaConfig c{T::BM, T::BN, T::BK, T::WGM, T::WGN, T::STAGES, T::STAGES == 2 ? 2 : 0,
+                 {}, {}, {}, {}, nullptr};
     fill_table<T, kFull>(c.full);
     fill_table<T, kPartial>(c.split);
     fill_pair<T, kAtomic, false, false>(c.atomic);
@@ -69,6 +72,7 @@ const MfmaConfig kMfmaConfigs[] = {
     make_cfg<MfmaTile<256, 128, 32, 2, 4>>(),  // 7
     make_cfg<MfmaTile<128, 64, 32, 2, 2>>(),   // 8
     make_cfg<MfmaTile<128, 128, 32, 4, 4>>(),  // 9
+    make_cfg<MfmaTile<128, 128, 16, 2, 4, 2>>(),  // 10: two-buffer ring, two workgroups per CU
 };
 constexpr int kNumMfmaConfigs = sizeof(kMfmaConfigs) / sizeof(kMfmaConfigs[0]);
 constexpr int kGroupM = 8;  // grouped-order height (the pages use groups of 8)
@@ -104,6 +108,14 @@ double tile_cost(int m, int n, int id, double efficiency) {
     return (double)per_cu * c.bm * c.bn / efficiency;
 }
 
+// Two resident workgroups of the two-buffer 128 x 128 tile (id 10) cover
+// each other's barrier waits; on MI355X that is 0.2-0.7 % faster than the
+// 16-wave tile once the grid runs 8 or more rounds of 128 x 128 tiles
+// (8192^3, 6144^3, 4096 x 8192 x 8192, 12288^2 x 4096, measured back to back
+// on one box), and slower on a grid of one to four rounds.
+constexpr int kTwoBufferId = 10;
+constexpr long long kTwoBufferMinRounds = 8;
+
 int choose_mfma_config(int m, int n, int k) {
     (void)k;
     int best = kCandidates[0].id;
@@ -115,6 +127,8 @@ int choose_mfma_config(int m, int n, int k) {
             best_cost = cost;
         }
     }
+    if (best == 9 && tile_count(m, n, kTwoBufferId) >= kTwoBufferMinRounds * kCUs)
+        best = kTwoBufferId;
     return best;
 }
 
@@ -164,13 +178,11 @@ constexpr double kCombineFixedUs = 3.0;
 constexpr double kCombineBytesPerUs = 6.0e6;
 constexpr size_t kAutoWorkspaceCap = size_t(512) << 20;  // automatic plans stay below this
 
+long long resident_per_cu(int config);
+
 double split_cost_us(int m, int n, const SplitPlan &sp, double efficiency) {
     const MfmaConfig &c = kMfmaConfigs[sp.config];
-    const long long lds = 3LL * (c.bm * c.bk + c.bk * c.bn) * 4;
-    const long long waves = (long long)c.wgm * c.wgn;
-    long long resident = (160LL * 1024) / lds;
-    if (resident > 32 / waves) resident = 32 / waves;
-    if (resident < 1) resident = 1;
+    const long long resident = resident_per_cu(sp.config);
     const long long per_cu = ceil_div(tile_count(m, n, sp.config) * sp.splits, kCUs);
     const double step_us = 2.0 * c.bm * c.bn * c.bk / 256.0 / efficiency / kClockMHz;
     double t = (double)per_cu *
@@ -186,14 +198,15 @@ double config_efficiency(int id) {
     return 0.9;
 }
 
-// Workgroups of configuration `config` one CU holds at once (LDS and wave
-// slots).
+// Workgroups of configuration `config` one CU holds at once (LDS, wave
+// slots, and the register budget the kernel was built for).
 long long resident_per_cu(int config) {
     const MfmaConfig &c = kMfmaConfigs[config];
-    const long long lds = 3LL * (c.bm * c.bk + c.bk * c.bn) * 4;
+    const long long lds = (long long)c.stages * (c.bm * c.bk + c.bk * c.bn) * 4;
     const long long waves = (long long)c.wgm * c.wgn;
     long long r = (160LL * 1024) / lds;
     if (r > 32 / waves) r = 32 / waves;
+    if (c.max_wgs > 0 && r > c.max_wgs) r = c.max_wgs;
     return r < 1 ? 1 : r;
 }
 

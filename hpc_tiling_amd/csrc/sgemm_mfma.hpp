@@ -53,12 +53,17 @@
 
 namespace mi {
 
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_>
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int STAGES_ = 3>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
-    static constexpr int STAGES = 3;                      // LDS buffers in the ring
+    static constexpr int STAGES = STAGES_;                // LDS buffers in the ring (2 or 3)
+    static constexpr int DIST = STAGES - 1;               // steps a load runs ahead
     static constexpr int WAVES = WGM * WGN;
     static constexpr int NT = 64 * WAVES;
+    // Waves per SIMD the register allocation must allow: one workgroup's
+    // share, or two workgroups' for a two-stage ring (whose barrier stalls
+    // the other resident workgroup covers).
+    static constexpr int WAVES_PER_SIMD = (WAVES + 3) / 4 * (STAGES == 2 ? 2 : 1);
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // per-wave tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 blocks per wave
     static constexpr int GROUPS = BK / 8;                 // groups of 8 k per step
@@ -66,6 +71,7 @@ struct MfmaTile {
     static_assert(GROUPS % 2 == 0, "fragment double-buffering needs an even group count");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
+    static_assert(STAGES == 2 || STAGES == 3, "ring of two or three buffers");
 };
 
 // Four floats of an e-contiguous fragment (read one by one).
@@ -217,9 +223,13 @@ __device__ __forceinline__ void load_lds4(const float *base, float *lds, int vof
 // ended it; buffer (t+1) % 3 was filled during step t-1 and completed by the
 // same barrier (which waits for the direct loads), so the first fragments of
 // step t+1 can be read before the barrier of step t and the MFMA stream does
-// not wait for LDS at a step boundary.
+// not wait for LDS at a step boundary.  A two-buffer ring (T::STAGES == 2)
+// loads one step ahead instead: buffer (t+1) % 2 was read during step t-1,
+// and step t+1's first fragments are read after the barrier of step t; the
+// other workgroup resident on the CU keeps the matrix cores busy meanwhile.
 template <class T, bool VEC, int MODE, bool TA = false, bool TB = false>
-__global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
+__global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
+void sgemm_mfma_kernel(GemmArgs p) {
     constexpr bool SPLIT = MODE == kPartial || MODE == kAtomic;
     using OA = Operand<T, T::BM, TA>;    // A: k-contiguous unless given transposed
     using OB = Operand<T, T::BN, !TB>;   // B: n-contiguous unless given transposed
@@ -228,10 +238,10 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
     // being read, and does not hold the MFMAs back until the load lands.
     __shared__ __attribute__((aligned(1024))) float As0[OA::ELEMS];
     __shared__ __attribute__((aligned(1024))) float As1[OA::ELEMS];
-    __shared__ __attribute__((aligned(1024))) float As2[OA::ELEMS];
+    __shared__ __attribute__((aligned(1024))) float As2[T::STAGES > 2 ? OA::ELEMS : 4];
     __shared__ __attribute__((aligned(1024))) float Bs0[OB::ELEMS];
     __shared__ __attribute__((aligned(1024))) float Bs1[OB::ELEMS];
-    __shared__ __attribute__((aligned(1024))) float Bs2[OB::ELEMS];
+    __shared__ __attribute__((aligned(1024))) float Bs2[T::STAGES > 2 ? OB::ELEMS : 4];
     auto a_buf = [&](auto s) -> float * {
         constexpr int S = decltype(s)::value;
         if constexpr (S == 0) return As0;
@@ -423,27 +433,28 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
                 store_regs(st, buf);
             }
         };
+        constexpr int NS = T::STAGES, D = T::DIST;
         fill(0, S0{});
-        if (nsteps > 1) fill(1, S1{});
+        if (D == 2 && nsteps > 1) fill(1, S1{});
         __syncthreads();
         read_frag(f[0], S0{}, 0);
 
-        // One step with its ring position CUR = step % 3 fixed at compile time.
-        // DIRECT: the tile two steps ahead is loaded directly (the steady
+        // One step with its ring position CUR = step % NS fixed at compile
+        // time.  DIRECT: the tile D steps ahead is loaded directly (the steady
         // state of interior tiles -- no VGPR loads in that loop, so the
         // compiler's wait counts never hold back the MFMAs); otherwise it goes
         // through VGPRs (edge tiles, unaligned operands, the last k steps).
         auto one_step = [&](int step, auto direct_tag, auto cur) {
             constexpr bool DIRECT = decltype(direct_tag)::value;
             constexpr int CUR = decltype(cur)::value;
-            using NXT = std::integral_constant<int, (CUR + 1) % 3>;  // (step + 1) % 3
-            using WRT = std::integral_constant<int, (CUR + 2) % 3>;  // (step + 2) % 3
-            const bool ahead = step + 2 < nsteps;
+            using NXT = std::integral_constant<int, (CUR + 1) % NS>;  // (step + 1) % NS
+            using WRT = std::integral_constant<int, (CUR + D) % NS>;  // (step + D) % NS
+            const bool ahead = step + D < nsteps;
             Stage st;
             if (DIRECT)
-                load_direct(step + 2, WRT{});
+                load_direct(step + D, WRT{});
             else if (ahead)
-                load_regs(st, step + 2);
+                load_regs(st, step + D);
             // The fences keep the scheduler from sinking the loads and the
             // next group's LDS reads below the MFMAs that hide them.
             __builtin_amdgcn_sched_barrier(0);
@@ -451,7 +462,7 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
             for (int g = 0; g < T::GROUPS; ++g) {
                 if (g + 1 < T::GROUPS) {
                     read_frag(f[(g + 1) & 1], cur, g + 1);
-                } else if (DIRECT || step + 1 < nsteps) {
+                } else if (D == 2 && (DIRECT || step + 1 < nsteps)) {
                     read_frag(f[0], NXT{}, 0);  // GROUPS is even: step+1 starts on set 0
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -460,25 +471,29 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs p) {
             }
             if (!DIRECT && ahead) store_regs(st, WRT{});
             __syncthreads();
+            // two buffers: step + 1's tile is complete only after the barrier
+            if (D == 1 && (DIRECT || step + 1 < nsteps)) read_frag(f[0], NXT{}, 0);
         };
         auto dispatch = [&](int step, auto direct_tag) {
-            switch (step % 3) {
+            switch (step % NS) {
                 case 0: one_step(step, direct_tag, S0{}); break;
                 case 1: one_step(step, direct_tag, S1{}); break;
-                default: one_step(step, direct_tag, std::integral_constant<int, 2>{}); break;
+                default:
+                    if constexpr (NS > 2) one_step(step, direct_tag, std::integral_constant<int, 2>{});
+                    break;
             }
         };
         using S2 = std::integral_constant<int, 2>;
         int step = 0;
-        // Steady state: three steps per iteration, so each ring position is a
+        // Steady state: NS steps per iteration, so each ring position is a
         // compile-time constant and the accumulators keep their registers
         // (a runtime switch per step makes the compiler copy them around).
-        for (; step + 4 < ndirect; step += 3) {
+        for (; step + NS - 1 + D < ndirect; step += NS) {
             one_step(step, std::true_type{}, S0{});
             one_step(step + 1, std::true_type{}, S1{});
-            one_step(step + 2, std::true_type{}, S2{});
+            if constexpr (NS > 2) one_step(step + 2, std::true_type{}, S2{});
         }
-        for (; step + 2 < ndirect; ++step) dispatch(step, std::true_type{});
+        for (; step + D < ndirect; ++step) dispatch(step, std::true_type{});
         for (; step < nsteps; ++step) dispatch(step, std::false_type{});
     }
     };
