@@ -441,17 +441,19 @@ void sgemm_mfma_kernel(GemmArgs p) {
 
         // One step with its ring position CUR = step % NS fixed at compile
         // time.  DIRECT: the tile D steps ahead is loaded directly (the steady
-        // state of interior tiles -- no VGPR loads in that loop, so the
-        // compiler's wait counts never hold back the MFMAs); otherwise it goes
-        // through VGPRs (edge tiles, unaligned operands, the last k steps).
+        // state -- no VGPR loads in that loop, so the compiler's wait counts
+        // never hold back the MFMAs); otherwise the step decides: directly
+        // while whole k steps remain, else through VGPRs (the partial last k
+        // step, or no direct loads at all), or nothing past the end.
         auto one_step = [&](int step, auto direct_tag, auto cur) {
             constexpr bool DIRECT = decltype(direct_tag)::value;
             constexpr int CUR = decltype(cur)::value;
             using NXT = std::integral_constant<int, (CUR + 1) % NS>;  // (step + 1) % NS
             using WRT = std::integral_constant<int, (CUR + D) % NS>;  // (step + D) % NS
             const bool ahead = step + D < nsteps;
+            const bool direct = DIRECT || step + D < ndirect;
             Stage st;
-            if (DIRECT)
+            if (direct)
                 load_direct(step + D, WRT{});
             else if (ahead)
                 load_regs(st, step + D);
@@ -469,21 +471,13 @@ void sgemm_mfma_kernel(GemmArgs p) {
                 mfma_group(f[g & 1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (!DIRECT && ahead) store_regs(st, WRT{});
+            if (!direct && ahead) store_regs(st, WRT{});
             __syncthreads();
             // two buffers: step + 1's tile is complete only after the barrier
             if (D == 1 && (DIRECT || step + 1 < nsteps)) read_frag(f[0], NXT{}, 0);
         };
-        auto dispatch = [&](int step, auto direct_tag) {
-            switch (step % NS) {
-                case 0: one_step(step, direct_tag, S0{}); break;
-                case 1: one_step(step, direct_tag, S1{}); break;
-                default:
-                    if constexpr (NS > 2) one_step(step, direct_tag, std::integral_constant<int, 2>{});
-                    break;
-            }
-        };
         using S2 = std::integral_constant<int, 2>;
+        using F = std::false_type;
         int step = 0;
         // Steady state: NS steps per iteration, so each ring position is a
         // compile-time constant and the accumulators keep their registers
@@ -493,8 +487,23 @@ void sgemm_mfma_kernel(GemmArgs p) {
             one_step(step + 1, std::true_type{}, S1{});
             if constexpr (NS > 2) one_step(step + 2, std::true_type{}, S2{});
         }
-        for (; step + D < ndirect; ++step) dispatch(step, std::true_type{});
-        for (; step < nsteps; ++step) dispatch(step, std::false_type{});
+        // Without direct loads (huge leading dimensions) whole rounds of the
+        // ring go through the deciding step too, so step % NS stays 0.
+        for (; nsteps - step > 5; step += NS) {
+            one_step(step, F{}, S0{});
+            one_step(step + 1, F{}, S1{});
+            if constexpr (NS > 2) one_step(step + 2, F{}, S2{});
+        }
+        // The last one to five steps, also at compile-time ring positions
+        // (step % NS == 0 here).
+        using Q3 = std::integral_constant<int, 3 % NS>;
+        using Q4 = std::integral_constant<int, 4 % NS>;
+        using Q2 = std::integral_constant<int, 2 % NS>;
+        if (step < nsteps) one_step(step, F{}, S0{});
+        if (step + 1 < nsteps) one_step(step + 1, F{}, S1{});
+        if (step + 2 < nsteps) one_step(step + 2, F{}, Q2{});
+        if (step + 3 < nsteps) one_step(step + 3, F{}, Q3{});
+        if (step + 4 < nsteps) one_step(step + 4, F{}, Q4{});
     }
     };
 
