@@ -251,8 +251,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU "
-              "(one MI355X); multi-GPU runs are out of scope.", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library and this benchmark "
+              "run on one GPU (one MI355X); multi-GPU runs are out of scope.", file=sys.stderr)
         return 2
 
     import torch

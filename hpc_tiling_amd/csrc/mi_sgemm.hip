@@ -9,7 +9,7 @@
 #include <cstring>
 
 #include "mi_sgemm.h"
-#include "sgemm_mfma.hpp"
+#include "mfma_configs.hpp"
 #include "sgemm_valu.hpp"
 #include "reduce.hpp"
 #include "splitk.hpp"
@@ -17,71 +17,22 @@
 namespace mi {
 namespace {
 
-using KernelFn = void (*)(GemmArgs);
-
 // ---------------------------------------------------------------------------
-// Tile configurations of the matrix-core kernel.
+// Tile configurations of the matrix-core kernel (mfma_configs.hpp).
 // ---------------------------------------------------------------------------
-// Kernel tables are indexed [trans_a][trans_b][vector loads].
-struct MfmaConfig {
-    int bm, bn, bk, wgm, wgn;
-    int stages;    // LDS buffers in the ring
-    int max_wgs;   // workgroups per CU the register budget allows (0: no limit beyond LDS and waves)
-    KernelFn full[2][2][2];   // full-k kernels
-    KernelFn split[2][2][2];  // split-K partial kernels
-    KernelFn atomic[2];       // split-K kernels adding into C atomically (operands as given)
-    KernelFn streamk[2][2][2];  // stream-K kernels
-    const void *fixup;          // stream-K fixup for this tile size
+const MfmaConfig *const kMfmaConfigTable[kNumMfmaConfigs] = {
+    &kMfmaConfig0, &kMfmaConfig1, &kMfmaConfig2, &kMfmaConfig3, &kMfmaConfig4, &kMfmaConfig5,
+    &kMfmaConfig6, &kMfmaConfig7, &kMfmaConfig8, &kMfmaConfig9, &kMfmaConfig10,
 };
+const MfmaConfig &mfma_config(int id) { return *kMfmaConfigTable[id]; }
 
-template <class T, int MODE, bool TA, bool TB>
-constexpr void fill_pair(KernelFn (&f)[2]) {
-    f[0] = &sgemm_mfma_kernel<T, false, MODE, TA, TB>;
-    f[1] = &sgemm_mfma_kernel<T, true, MODE, TA, TB>;
-}
-
-template <class T, int MODE>
-constexpr void fill_table(KernelFn (&f)[2][2][2]) {
-    fill_pair<T, MODE, false, false>(f[0][0]);
-    fill_pair<T, MODE, false, true>(f[0][1]);
-    fill_pair<T, MODE, true, false>(f[1][0]);
-    fill_pair<T, MODE, true, true>(f[1][1]);
-}
-
-template <class T>
-constexpr MfmaConfig make_cfg() {
-    MfmaConfig c{T::BM, T::BN, T::BK, T::WGM, T::WGN, T::STAGES, T::STAGES == 2 ? 2 : 0,
-                 {}, {}, {}, {}, nullptr};
-    fill_table<T, kFull>(c.full);
-    fill_table<T, kPartial>(c.split);
-    fill_pair<T, kAtomic, false, false>(c.atomic);
-    fill_table<T, kStreamK>(c.streamk);
-    c.fixup = reinterpret_cast<const void *>(&streamk_fixup_kernel<T::BM, T::BN>);
-    return c;
-}
-
-// MfmaTile<BM, BN, BK, waves along m, waves along n>
-const MfmaConfig kMfmaConfigs[] = {
-    make_cfg<MfmaTile<128, 128, 16, 2, 2>>(),  // 0
-    make_cfg<MfmaTile<128, 128, 32, 2, 2>>(),  // 1
-    make_cfg<MfmaTile<128, 128, 16, 2, 4>>(),  // 2
-    make_cfg<MfmaTile<128, 128, 32, 2, 4>>(),  // 3
-    make_cfg<MfmaTile<256, 128, 16, 2, 4>>(),  // 4
-    make_cfg<MfmaTile<128, 256, 16, 2, 4>>(),  // 5
-    make_cfg<MfmaTile<64, 64, 32, 2, 2>>(),    // 6
-    make_cfg<MfmaTile<256, 128, 32, 2, 4>>(),  // 7
-    make_cfg<MfmaTile<128, 64, 32, 2, 2>>(),   // 8
-    make_cfg<MfmaTile<128, 128, 32, 4, 4>>(),  // 9
-    make_cfg<MfmaTile<128, 128, 16, 2, 4, 2>>(),  // 10: two-buffer ring, two workgroups per CU
-};
-constexpr int kNumMfmaConfigs = sizeof(kMfmaConfigs) / sizeof(kMfmaConfigs[0]);
 constexpr int kGroupM = 8;  // grouped-order height (the pages use groups of 8)
 constexpr int kCUs = 256;   // MI355X compute units
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 long long tile_count(int m, int n, int id) {
-    return ceil_div(m, kMfmaConfigs[id].bm) * ceil_div(n, kMfmaConfigs[id].bn);
+    return ceil_div(m, mfma_config(id).bm) * ceil_div(n, mfma_config(id).bn);
 }
 
 // Tile choice: a small cost model.  The workgroups of a launch are spread
@@ -103,7 +54,7 @@ constexpr Candidate kCandidates[] = {
 };
 
 double tile_cost(int m, int n, int id, double efficiency) {
-    const MfmaConfig &c = kMfmaConfigs[id];
+    const MfmaConfig &c = mfma_config(id);
     const long long per_cu = ceil_div(tile_count(m, n, id), kCUs);
     return (double)per_cu * c.bm * c.bn / efficiency;
 }
@@ -155,7 +106,7 @@ constexpr size_t kWsAlign = 256;
 SplitPlan make_plan(int m, int n, int k, long long want, int config) {
     SplitPlan sp{config, 0, 0, 0, 0, 0, 0, 0};
     if (m <= 0 || n <= 0 || k <= 0) return sp;
-    const MfmaConfig &c = kMfmaConfigs[config];
+    const MfmaConfig &c = mfma_config(config);
     const long long kps = ceil_div(ceil_div(k, want), c.bk) * c.bk;
     sp.k_per_split = (int)kps;
     sp.splits = (int)ceil_div(k, kps);
@@ -181,7 +132,7 @@ constexpr size_t kAutoWorkspaceCap = size_t(512) << 20;  // automatic plans stay
 long long resident_per_cu(int config);
 
 double split_cost_us(int m, int n, const SplitPlan &sp, double efficiency) {
-    const MfmaConfig &c = kMfmaConfigs[sp.config];
+    const MfmaConfig &c = mfma_config(sp.config);
     const long long resident = resident_per_cu(sp.config);
     const long long per_cu = ceil_div(tile_count(m, n, sp.config) * sp.splits, kCUs);
     const double step_us = 2.0 * c.bm * c.bn * c.bk / 256.0 / efficiency / kClockMHz;
@@ -201,7 +152,7 @@ double config_efficiency(int id) {
 // Workgroups of configuration `config` one CU holds at once (LDS, wave
 // slots, and the register budget the kernel was built for).
 long long resident_per_cu(int config) {
-    const MfmaConfig &c = kMfmaConfigs[config];
+    const MfmaConfig &c = mfma_config(config);
     const long long lds = (long long)c.stages * (c.bm * c.bk + c.bk * c.bn) * 4;
     const long long waves = (long long)c.wgm * c.wgn;
     long long r = (160LL * 1024) / lds;
@@ -222,7 +173,7 @@ long long resident_per_cu(int config) {
 SplitPlan make_sk_plan(int m, int n, int k, int config, long long grid) {
     SplitPlan sp{config, 1, k, 0, 0, 0, 0, 0, 0};
     if (m <= 0 || n <= 0 || k <= 0) return sp;
-    const MfmaConfig &c = kMfmaConfigs[config];
+    const MfmaConfig &c = mfma_config(config);
     const long long ksteps = ceil_div(k, c.bk);
     const long long tiles = tile_count(m, n, config);
     if (grid <= 0) grid = kCUs * resident_per_cu(config);
@@ -250,7 +201,7 @@ SplitPlan make_sk_plan(int m, int n, int k, int config, long long grid) {
 double sk_cost_us(int m, int n, const SplitPlan &sp, double efficiency) {
     (void)m;
     (void)n;
-    const MfmaConfig &c = kMfmaConfigs[sp.config];
+    const MfmaConfig &c = mfma_config(sp.config);
     const double step_us = 2.0 * c.bm * c.bn * c.bk / 256.0 / efficiency / kClockMHz;
     const long long rounds = sp.sk_dp_tiles / sp.sk_grid;
     const long long share = ceil_div(sp.sk_iters, sp.sk_grid);
@@ -294,7 +245,7 @@ SplitPlan plan_split(int m, int n, int k, int splits, int config, bool allow_sk 
             consider(id, splits);
             continue;
         }
-        const long long ksteps = ceil_div(k, kMfmaConfigs[id].bk);
+        const long long ksteps = ceil_div(k, mfma_config(id).bk);
         for (long long want = 1; want <= 256 && want <= ksteps; want += (want < 32 ? 1 : 4))
             consider(id, want);
         // stream-K, when every workgroup's share spans at least a quarter of
@@ -413,7 +364,7 @@ int prologue(int m, int n, int k, float alpha, const float *A, int lda, const fl
 // The full-k matrix-core kernel of configuration `id` (arguments checked).
 int launch_full(int id, int ta, int tb, int m, int n, int k, float alpha, const float *A, int lda,
                 const float *B, int ldb, float beta, float *C, int ldc, hipStream_t s) {
-    const MfmaConfig &c = kMfmaConfigs[id];
+    const MfmaConfig &c = mfma_config(id);
     GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
     a.tiles_m = (int)ceil_div(m, c.bm);
     a.tiles_n = (int)ceil_div(n, c.bn);
@@ -453,7 +404,7 @@ int launch_streamk(const SplitPlan &sp, int ta, int tb, int m, int n, int k, flo
                    int ldc, void *ws, hipStream_t s) {
     float *wsa = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + kWsAlign - 1) &
                                            ~(uintptr_t)(kWsAlign - 1));
-    const MfmaConfig &c = kMfmaConfigs[sp.config];
+    const MfmaConfig &c = mfma_config(sp.config);
     GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
     a.tiles_m = (int)ceil_div(m, c.bm);
     a.tiles_n = (int)ceil_div(n, c.bn);
@@ -499,7 +450,7 @@ int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, con
 
     float *wsa = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(ws) + kWsAlign - 1) &
                                            ~(uintptr_t)(kWsAlign - 1));
-    const MfmaConfig &c = kMfmaConfigs[id];
+    const MfmaConfig &c = mfma_config(id);
     GemmArgs a = base_args(m, n, k, 1.f, A, lda, B, ldb, 0.f, nullptr, ldc);
     a.tiles_m = (int)ceil_div(m, c.bm);
     a.tiles_n = (int)ceil_div(n, c.bn);
@@ -541,7 +492,7 @@ int run_splitk_atomic(int config, int m, int n, int k, float alpha, const float 
         st = launch_scale(m, n, beta, C, ldc, s);
         if (st) return st;
     }
-    const MfmaConfig &c = kMfmaConfigs[id];
+    const MfmaConfig &c = mfma_config(id);
     GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
     a.tiles_m = (int)ceil_div(m, c.bm);
     a.tiles_n = (int)ceil_div(n, c.bn);
@@ -783,7 +734,7 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
             if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
             id = config < 0 ? choose_mfma_config(m, n, k) : config;
         }
-        const MfmaConfig &c = kMfmaConfigs[id];
+        const MfmaConfig &c = mfma_config(id);
         plan->config = id;
         plan->tile_m = c.bm; plan->tile_n = c.bn; plan->tile_k = c.bk;
         plan->micro_m = c.bm / c.wgm; plan->micro_n = c.bn / c.wgn;

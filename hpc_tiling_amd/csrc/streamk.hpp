@@ -1,0 +1,103 @@
+// streamk.hpp -- the fixup kernel of the stream-K schedule (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace mi {
+
+// Stream-K fixup over the shared tiles tile0, tile0 + 1, ... (`iters` is
+// their count times `ksteps`).  Blocks come in groups of kFixupSplit, one per
+// band of rows of a tile.  Group b - 1 (b = 1 .. grid - 1) looks at the
+// iteration where workgroup b's range starts; if that is inside a tile, and b
+// is the first workgroup starting inside it, the tile was shared: its parts
+// sit in the slots of workgroups first .. last (the owners of the tile's first
+// and last iterations), and the group adds them in that order -- which is
+// also k order, so the result is fixed -- then writes C = alpha * sum +
+// beta * C.  At most kFixupMaxParts workgroups may share one tile (the host
+// keeps the grid below that).
+constexpr int kFixupMaxParts = 2048;
+constexpr int kFixupSplit = 4;
+constexpr int kFixupThreads = 256;
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kFixupThreads) void streamk_fixup_kernel(
+    const float *__restrict__ ws, long long iters, int ksteps, int grid, int tile0, int tiles_m,
+    int tiles_n, int group_m, int m, int n, float alpha, float beta, float *C, long long ldc) {
+    const long long b = (long long)(blockIdx.x / kFixupSplit) + 1;
+    const int band = blockIdx.x % kFixupSplit;
+    const long long x = sk_begin(b, iters, grid);
+    if (x >= iters || x % ksteps == 0) return;
+    const long long t = x / ksteps;
+    const long long first = sk_owner(t * ksteps, iters, grid);
+    if (first + 1 != b) return;
+    const long long last = sk_owner(t * ksteps + ksteps - 1, iters, grid);
+    const int parts = (int)(last - first + 1);
+
+    // slot offset of every part (-1: a workgroup with an empty range)
+    __shared__ long long part_off[kFixupMaxParts];
+    for (int q = threadIdx.x; q < parts; q += kFixupThreads) {
+        const long long w = first + q;
+        const long long wb = sk_begin(w, iters, grid);
+        part_off[q] = sk_begin(w + 1, iters, grid) == wb
+                          ? -1
+                          : (w * 2 + (wb > t * ksteps ? 0 : 1)) * (long long)(BM * BN);
+    }
+    __syncthreads();
+
+    // Lane l of band j holds float4 groups j * BAND + l, j * BAND + l + 256,
+    // ... of the tile (row-major, BN a multiple of 4).  The parts are added in
+    // order, two parts' loads in flight together.  Entries of the slots
+    // outside C's extent were never written and are not stored.
+    constexpr int BAND = BM * BN / 4 / kFixupSplit;
+    constexpr int PER = BAND / kFixupThreads;
+    static_assert(PER >= 1 && BAND % kFixupThreads == 0, "a band must fill the block");
+    const int g0 = band * BAND + threadIdx.x;
+    auto part = [&](long long off, int u) -> f32x4 {
+        if (off < 0) return f32x4{0.f, 0.f, 0.f, 0.f};
+        return reinterpret_cast<const f32x4 *>(ws + off)[g0 + u * kFixupThreads];
+    };
+    f32x4 acc[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int q = 0;
+    for (; q + 1 < parts; q += 2) {
+        const long long o0 = part_off[q], o1 = part_off[q + 1];
+        f32x4 v0[PER], v1[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            v0[u] = part(o0, u);
+            v1[u] = part(o1, u);
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            acc[u] += v0[u];
+            acc[u] += v1[u];
+        }
+    }
+    if (q < parts) {
+        const long long o0 = part_off[q];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) acc[u] += part(o0, u);
+    }
+    int tm, tn;
+    grouped_tile(tile0 + (int)t, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int e = 4 * (g0 + u * kFixupThreads);
+        const int row = m0 + e / BN, col = n0 + e % BN;
+        if (row >= m) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (col + j >= n) break;
+            float *dst = C + (long long)row * ldc + col + j;
+            float v = alpha * acc[u][j];
+            if (beta != 0.f) v = __builtin_fmaf(beta, *dst, v);
+            *dst = v;
+        }
+    }
+}
+
+}  // namespace mi
