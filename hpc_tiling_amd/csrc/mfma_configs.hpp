@@ -64,13 +64,15 @@ template <> struct TileOf<6> { using type = MfmaTile<64, 64, 32, 2, 2>; };
 template <> struct TileOf<7> { using type = MfmaTile<256, 128, 32, 2, 4>; };
 template <> struct TileOf<8> { using type = MfmaTile<128, 64, 32, 2, 2>; };
 template <> struct TileOf<9> { using type = MfmaTile<128, 128, 32, 4, 4>; };
-// two-buffer ring, two workgroups per CU
+// two-buffer rings, two workgroups per CU
 template <> struct TileOf<10> { using type = MfmaTile<128, 128, 16, 2, 4, 2>; };
-constexpr int kNumMfmaConfigs = 11;
+template <> struct TileOf<11> { using type = MfmaTile<128, 128, 32, 4, 2, 2>; };
+constexpr int kNumMfmaConfigs = 12;
 
 // One table per configuration, each defined (constant-initialised) in its
 // own build of mfma_cfg.hip.
 extern const MfmaConfig kMfmaConfig0, kMfmaConfig1, kMfmaConfig2, kMfmaConfig3, kMfmaConfig4,
-    kMfmaConfig5, kMfmaConfig6, kMfmaConfig7, kMfmaConfig8, kMfmaConfig9, kMfmaConfig10;
+    kMfmaConfig5, kMfmaConfig6, kMfmaConfig7, kMfmaConfig8, kMfmaConfig9, kMfmaConfig10,
+    kMfmaConfig11;
 
 }  // namespace mi

@@ -22,7 +22,7 @@ namespace {
 // ---------------------------------------------------------------------------
 const MfmaConfig *const kMfmaConfigTable[kNumMfmaConfigs] = {
     &kMfmaConfig0, &kMfmaConfig1, &kMfmaConfig2, &kMfmaConfig3, &kMfmaConfig4, &kMfmaConfig5,
-    &kMfmaConfig6, &kMfmaConfig7, &kMfmaConfig8, &kMfmaConfig9, &kMfmaConfig10,
+    &kMfmaConfig6, &kMfmaConfig7, &kMfmaConfig8, &kMfmaConfig9, &kMfmaConfig10, &kMfmaConfig11,
 };
 const MfmaConfig &mfma_config(int id) { return *kMfmaConfigTable[id]; }
 
@@ -59,12 +59,13 @@ double tile_cost(int m, int n, int id, double efficiency) {
     return (double)per_cu * c.bm * c.bn / efficiency;
 }
 
-// Two resident workgroups of the two-buffer 128 x 128 tile (id 10) cover
-// each other's barrier waits; on MI355X that is 0.2-0.7 % faster than the
-// 16-wave tile once the grid runs 8 or more rounds of 128 x 128 tiles
-// (8192^3, 6144^3, 4096 x 8192 x 8192, 12288^2 x 4096, measured back to back
-// on one box), and slower on a grid of one to four rounds.
-constexpr int kTwoBufferId = 10;
+// Two resident workgroups of a two-buffer 128 x 128 x 32 tile (id 11, 8
+// waves in a 4 x 2 layout) cover each other's barrier waits; on MI355X that
+// is 0.6-1.0 % faster than the 16-wave tile once the grid runs 8 or more
+// rounds of 128 x 128 tiles (8192^3, 8192^2 x 4096, 6144^3,
+// 4096 x 8192 x 8192, 12288^2 x 4096, measured back to back on one box),
+// level at four rounds and slower on one.
+constexpr int kTwoBufferId = 11;
 constexpr long long kTwoBufferMinRounds = 8;
 
 int choose_mfma_config(int m, int n, int k) {
