@@ -42,7 +42,7 @@ constexpr void fill_table(KernelFn (&f)[2][2][2]) {
 
 template <class T>
 constexpr MfmaConfig make_cfg() {
-    MfmaConfig c{T::BM, T::BN, T::BK, T::WGM, T::WGN, T::STAGES, T::STAGES == 2 ? 2 : 0,
+    MfmaConfig c{T::BM, T::BN, T::BK, T::WGM, T::WGN, T::STAGES, T::WGS > 1 ? T::WGS : 0,
                  {}, {}, {}, {}, nullptr};
     fill_table<T, kFull>(c.full);
     fill_table<T, kPartial>(c.split);
@@ -67,12 +67,14 @@ template <> struct TileOf<9> { using type = MfmaTile<128, 128, 32, 4, 4>; };
 // two-buffer rings, two workgroups per CU
 template <> struct TileOf<10> { using type = MfmaTile<128, 128, 16, 2, 4, 2>; };
 template <> struct TileOf<11> { using type = MfmaTile<128, 128, 32, 4, 2, 2>; };
-constexpr int kNumMfmaConfigs = 12;
+// 64 x 64 x 16 built for six workgroups per CU
+template <> struct TileOf<12> { using type = MfmaTile<64, 64, 16, 2, 2, 3, 6>; };
+constexpr int kNumMfmaConfigs = 13;
 
 // One table per configuration, each defined (constant-initialised) in its
 // own build of mfma_cfg.hip.
 extern const MfmaConfig kMfmaConfig0, kMfmaConfig1, kMfmaConfig2, kMfmaConfig3, kMfmaConfig4,
     kMfmaConfig5, kMfmaConfig6, kMfmaConfig7, kMfmaConfig8, kMfmaConfig9, kMfmaConfig10,
-    kMfmaConfig11;
+    kMfmaConfig11, kMfmaConfig12;
 
 }  // namespace mi

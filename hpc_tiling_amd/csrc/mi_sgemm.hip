@@ -23,6 +23,7 @@ namespace {
 const MfmaConfig *const kMfmaConfigTable[kNumMfmaConfigs] = {
     &kMfmaConfig0, &kMfmaConfig1, &kMfmaConfig2, &kMfmaConfig3, &kMfmaConfig4, &kMfmaConfig5,
     &kMfmaConfig6, &kMfmaConfig7, &kMfmaConfig8, &kMfmaConfig9, &kMfmaConfig10, &kMfmaConfig11,
+    &kMfmaConfig12,
 };
 const MfmaConfig &mfma_config(int id) { return *kMfmaConfigTable[id]; }
 
@@ -68,6 +69,15 @@ double tile_cost(int m, int n, int id, double efficiency) {
 constexpr int kTwoBufferId = 11;
 constexpr long long kTwoBufferMinRounds = 8;
 
+// When k leaves a partial 32-wide step, the 64 x 64 x 16 tile built for six
+// workgroups per CU (id 12) beats the 64 x 64 x 32 one on grids of 8 or more
+// rounds of 64 x 64 tiles: 3001 x 4997 x 1023 +4 %, 5000^2 x 2047 +4 %,
+// 3000^2 x 700 +3 %, 2500 x 6000 x 777 with unaligned rows +15 % (back to
+// back on one MI355X).  With a whole number of 32-wide steps, or a short
+// grid (1000^3: -3 %), it loses.
+constexpr int kSmallStepId = 12;
+constexpr long long kSmallStepMinRounds = 8;
+
 int choose_mfma_config(int m, int n, int k) {
     (void)k;
     int best = kCandidates[0].id;
@@ -81,6 +91,8 @@ int choose_mfma_config(int m, int n, int k) {
     }
     if (best == 9 && tile_count(m, n, kTwoBufferId) >= kTwoBufferMinRounds * kCUs)
         best = kTwoBufferId;
+    if (best == 6 && k % 32 != 0 && tile_count(m, n, kSmallStepId) >= kSmallStepMinRounds * kCUs)
+        best = kSmallStepId;
     return best;
 }
 

@@ -53,17 +53,19 @@
 
 namespace mi {
 
-template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int STAGES_ = 3>
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int STAGES_ = 3,
+          int WGS_ = (STAGES_ == 2 ? 2 : 1)>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
     static constexpr int STAGES = STAGES_;                // LDS buffers in the ring (2 or 3)
     static constexpr int DIST = STAGES - 1;               // steps a load runs ahead
     static constexpr int WAVES = WGM * WGN;
     static constexpr int NT = 64 * WAVES;
-    // Waves per SIMD the register allocation must allow: one workgroup's
-    // share, or two workgroups' for a two-stage ring (whose barrier stalls
-    // the other resident workgroup covers).
-    static constexpr int WAVES_PER_SIMD = (WAVES + 3) / 4 * (STAGES == 2 ? 2 : 1);
+    // Workgroups per CU the register allocation must allow (a two-stage ring
+    // relies on another resident workgroup to cover its barrier stalls), and
+    // the waves per SIMD that makes.
+    static constexpr int WGS = WGS_;
+    static constexpr int WAVES_PER_SIMD = (WAVES * WGS + 3) / 4;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // per-wave tile
     static constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 blocks per wave
     static constexpr int GROUPS = BK / 8;                 // groups of 8 k per step
@@ -205,6 +207,9 @@ __device__ __forceinline__ void load_lds4(const float *base, float *lds, int vof
                                                         kBufferWord3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds), 4, voffset, 0, 0, 0);
 }
+
+// What a step loads for the step DIST ahead (see one_step in the kernel).
+constexpr int kLoadNone = 0, kLoadDirect = 1, kLoadRegs = 2, kLoadAuto = 3;
 
 // Epilogue modes.  kFull: the whole k range, C = alpha*acc + beta*C.
 // kPartial: workgroup (tile, slice) sums k in [slice*k_per_split, ...) into
@@ -445,13 +450,16 @@ void sgemm_mfma_kernel(GemmArgs p) {
         // never hold back the MFMAs); otherwise the step decides: directly
         // while whole k steps remain, else through VGPRs (the partial last k
         // step, or no direct loads at all), or nothing past the end.
-        auto one_step = [&](int step, auto direct_tag, auto cur) {
-            constexpr bool DIRECT = decltype(direct_tag)::value;
+        // LOAD: what the step loads for step + D -- kLoadDirect, kLoadRegs
+        // (the partial last k step), kLoadNone (past the end), or kLoadAuto
+        // (decided at run time).
+        auto one_step = [&](int step, auto load_tag, auto cur) {
+            constexpr int LOAD = decltype(load_tag)::value;
             constexpr int CUR = decltype(cur)::value;
             using NXT = std::integral_constant<int, (CUR + 1) % NS>;  // (step + 1) % NS
             using WRT = std::integral_constant<int, (CUR + D) % NS>;  // (step + D) % NS
-            const bool ahead = step + D < nsteps;
-            const bool direct = DIRECT || step + D < ndirect;
+            const bool ahead = LOAD == kLoadAuto ? step + D < nsteps : LOAD != kLoadNone;
+            const bool direct = LOAD == kLoadAuto ? step + D < ndirect : LOAD == kLoadDirect;
             Stage st;
             if (direct)
                 load_direct(step + D, WRT{});
@@ -462,9 +470,11 @@ void sgemm_mfma_kernel(GemmArgs p) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int g = 0; g < T::GROUPS; ++g) {
+                // (the last step reads the next buffer too: stale, unused, and
+                // without a branch in front of the last MFMA group)
                 if (g + 1 < T::GROUPS) {
                     read_frag(f[(g + 1) & 1], cur, g + 1);
-                } else if (D == 2 && (DIRECT || step + 1 < nsteps)) {
+                } else if (D == 2) {
                     read_frag(f[0], NXT{}, 0);  // GROUPS is even: step+1 starts on set 0
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -474,36 +484,82 @@ void sgemm_mfma_kernel(GemmArgs p) {
             if (!direct && ahead) store_regs(st, WRT{});
             __syncthreads();
             // two buffers: step + 1's tile is complete only after the barrier
-            if (D == 1 && (DIRECT || step + 1 < nsteps)) read_frag(f[0], NXT{}, 0);
+            if (D == 1) read_frag(f[0], NXT{}, 0);
         };
         using S2 = std::integral_constant<int, 2>;
-        using F = std::false_type;
+        using LD = std::integral_constant<int, kLoadDirect>;
+        using LA = std::integral_constant<int, kLoadAuto>;
         int step = 0;
         // Steady state: NS steps per iteration, so each ring position is a
         // compile-time constant and the accumulators keep their registers
         // (a runtime switch per step makes the compiler copy them around).
         for (; step + NS - 1 + D < ndirect; step += NS) {
-            one_step(step, std::true_type{}, S0{});
-            one_step(step + 1, std::true_type{}, S1{});
-            if constexpr (NS > 2) one_step(step + 2, std::true_type{}, S2{});
+            one_step(step, LD{}, S0{});
+            one_step(step + 1, LD{}, S1{});
+            if constexpr (NS > 2) one_step(step + 2, LD{}, S2{});
         }
         // Without direct loads (huge leading dimensions) whole rounds of the
         // ring go through the deciding step too, so step % NS stays 0.
         for (; nsteps - step > 5; step += NS) {
-            one_step(step, F{}, S0{});
-            one_step(step + 1, F{}, S1{});
-            if constexpr (NS > 2) one_step(step + 2, F{}, S2{});
+            one_step(step, LA{}, S0{});
+            one_step(step + 1, LA{}, S1{});
+            if constexpr (NS > 2) one_step(step + 2, LA{}, S2{});
         }
-        // The last one to five steps, also at compile-time ring positions
-        // (step % NS == 0 here).
-        using Q3 = std::integral_constant<int, 3 % NS>;
-        using Q4 = std::integral_constant<int, 4 % NS>;
-        using Q2 = std::integral_constant<int, 2 % NS>;
-        if (step < nsteps) one_step(step, F{}, S0{});
-        if (step + 1 < nsteps) one_step(step + 1, F{}, S1{});
-        if (step + 2 < nsteps) one_step(step + 2, F{}, Q2{});
-        if (step + 3 < nsteps) one_step(step + 3, F{}, Q3{});
-        if (step + 4 < nsteps) one_step(step + 4, F{}, Q4{});
+        // The last R <= 5 steps (step % NS == 0 here), ND of them whole k
+        // steps, as one of a few sequences fixed at compile time: step i
+        // loads step i + D directly, through VGPRs (the partial step) or not
+        // at all.  Decided in each step at run time, they ran about a
+        // quarter of a step slower each.
+        auto tail = [&](auto r_tag, auto nd_tag) {
+            constexpr int R = decltype(r_tag)::value, ND = decltype(nd_tag)::value;
+            auto at = [&](auto i_tag) {
+                constexpr int I = decltype(i_tag)::value;
+                if constexpr (I < R) {
+                    constexpr int L = I + D >= R ? kLoadNone : (I + D < ND ? kLoadDirect : kLoadRegs);
+                    one_step(step + I, std::integral_constant<int, L>{},
+                             std::integral_constant<int, I % NS>{});
+                }
+            };
+            at(std::integral_constant<int, 0>{});
+            at(std::integral_constant<int, 1>{});
+            at(std::integral_constant<int, 2>{});
+            at(std::integral_constant<int, 3>{});
+            at(std::integral_constant<int, 4>{});
+        };
+        auto tail_auto = [&]() {
+            using Q2 = std::integral_constant<int, 2 % NS>;
+            using Q3 = std::integral_constant<int, 3 % NS>;
+            using Q4 = std::integral_constant<int, 4 % NS>;
+            if (step < nsteps) one_step(step, LA{}, S0{});
+            if (step + 1 < nsteps) one_step(step + 1, LA{}, S1{});
+            if (step + 2 < nsteps) one_step(step + 2, LA{}, Q2{});
+            if (step + 3 < nsteps) one_step(step + 3, LA{}, Q3{});
+            if (step + 4 < nsteps) one_step(step + 4, LA{}, Q4{});
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        using I4 = std::integral_constant<int, 4>;
+        using I5 = std::integral_constant<int, 5>;
+        const int rem = nsteps - step, nd = ndirect - step;
+        // (rem, nd): nd is rem or rem - 1 when direct loads are used, and at
+        // most 2 * NS - 2 after the steady loop.  Two-buffer rings (long k
+        // steps per tile, registers to the limit) keep the run-time tail.
+        if constexpr (NS == 2) {
+            tail_auto();
+        } else switch (rem * 8 + nd) {
+            case 1 * 8 + 0: tail(I1{}, I0{}); break;
+            case 1 * 8 + 1: tail(I1{}, I1{}); break;
+            case 2 * 8 + 1: tail(I2{}, I1{}); break;
+            case 2 * 8 + 2: tail(I2{}, I2{}); break;
+            case 3 * 8 + 2: tail(I3{}, I2{}); break;
+            case 3 * 8 + 3: tail(I3{}, I3{}); break;
+            case 4 * 8 + 3: tail(I4{}, I3{}); break;
+            case 4 * 8 + 4: tail(I4{}, I4{}); break;
+            case 5 * 8 + 4: tail(I5{}, I4{}); break;
+            default: tail_auto(); break;
+        }
     }
     };
 
