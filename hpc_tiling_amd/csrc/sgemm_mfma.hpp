@@ -4,11 +4,13 @@
 // 基于 register 计算 and prefetch 和双缓冲, re-planned for gfx950):
 //   * a workgroup of WGM x WGN waves owns a BM x BN tile of C and walks k in
 //     steps of BK ("big iterations");
-//   * each step stages a BM x BK tile of A and a BK x BN tile of B in one of
-//     three LDS buffers.  Whole k steps use gfx950's direct global->LDS
-//     loads (buffer_load_dwordx4 ... lds, 16 bytes per lane, for aligned
-//     operands; buffer_load_dword ... lds, 4 bytes per lane, otherwise; no
-//     VGPRs involved), issued two steps ahead; the partial last k step (and
+//   * each step stages a BM x BK tile of A and a BK x BN tile of B in a ring
+//     of three LDS buffers (two for tiles built for two workgroups per CU).
+//     Whole k steps use gfx950's direct global->LDS loads
+//     (buffer_load_dwordx4 ... lds, 16 bytes per lane, for aligned operands;
+//     buffer_load_dword ... lds, 4 bytes per lane, otherwise; no VGPRs
+//     involved), issued two steps ahead (one with two buffers); the partial
+//     last k step (and
 //     tiles whose byte offsets exceed the buffer range) use masked 16-byte
 //     or element loads through VGPRs with out-of-range elements stored as
 //     zeros (page aerisun.top, section "Shared Tiling 与 block 内复用");
@@ -216,7 +218,10 @@ constexpr int kLoadNone = 0, kLoadDirect = 1, kLoadRegs = 2, kLoadAuto = 3;
 // the raw partial ws[slice] (no alpha/beta).  kAtomic: the same slice sum,
 // added as alpha*acc to C with hardware float atomics (C already holds
 // beta*C; the order of the additions, hence the last bits, varies from run
-// to run).  VEC: A and B allow 16-byte loads.
+// to run).  kStreamK: whole tiles, then even shares of the (tile, k step)
+// iterations of the rest, cut tiles left in workspace slots for the fixup
+// kernel (see the stream-K branch at the end).  VEC: A and B allow 16-byte
+// loads.
 //
 // Pipeline (one barrier per step, buffers used round-robin):
 //   top of step t    issue the tile of step t+2 into buffer (t+2) % 3 (direct
