@@ -298,3 +298,28 @@ def test_splitk_atomic_beta_one_and_tolerance(orc):
     w = synth.workload(3).scaled(dist_c="uniform", alpha=-0.5, beta=1.0)
     sampled_check(orc, "splitk_atomic", w, integer=False, nrows=16)
     sampled_check(orc, "splitk_atomic", w, integer=True, nrows=16)
+
+
+# ---------------------------------------------------------------------------
+# Every ending of the k loop on every tile configuration
+# ---------------------------------------------------------------------------
+def k_loop_values(bk):
+    """k values with 1..9 k steps of the tile, whole or with a partial last
+    step: the steady loop stops one to five steps before the end, and the
+    steps after it run as one of several fixed sequences chosen by how many
+    steps remain and how many of them are whole."""
+    return sorted({j * bk + r for j in range(9) for r in (1, bk - 1, bk) if j * bk + r > 0})
+
+
+@pytest.mark.parametrize("aligned", [True, False], ids=["ld16B", "ld_odd"])
+@pytest.mark.parametrize("config", range(N_MFMA_CFG))
+def test_k_loop_endings(orc, config, aligned):
+    bk = hta.mi_sgemm_get_plan(hta.KERNEL_MFMA, config, 64, 64, 64, 0)["tile_k"]
+    m, n = 70, 66
+    for k in k_loop_values(bk):
+        if aligned:
+            lda, ldb = (k + 3) // 4 * 4 + 4, n + 2
+        else:
+            lda, ldb = (k + 1 if (k + 1) % 4 else k + 2), n + 1
+        w = synth.Workload(9, "kloop", m, n, k, lda, ldb, n + 3, "uniform", "int3", 1.5, -0.5)
+        full_check(orc, f"mfma_cfg{config}", w, integer=True)
