@@ -124,3 +124,15 @@ def test_streamk_deterministic_and_auto_plan(orc):
     ref = orc.sgemm(m, n, k, 1.0, A, k, B, n, 0.0, C, n, rows=rows, want_g=True)
     assert_close(C1.cpu().numpy()[rows], ref["C"].reshape(m, n)[rows], ref["G"], 1.0, 0.0, 0.0,
                  "auto stream-K")
+
+
+# Segments that start and stop at every offset of the k loop: a small grid
+# cuts tiles at many (tile, k step) positions, and k runs over whole and
+# partial last steps.
+@pytest.mark.parametrize("config", [6, 9, 12])
+def test_streamk_k_sweep(orc, config):
+    bk = hta.mi_sgemm_get_plan(hta.KERNEL_MFMA, config, 64, 64, 64, 0)["tile_k"]
+    for k in sorted({j * bk + r for j in (1, 2, 3, 5, 8) for r in (0, 1, bk - 1)}):
+        w = synth.Workload(10, "skk", 150, 140, k, k + 4, 144, 141, "uniform", "int3", 1.0, 0.5)
+        for grid in (3, 7):
+            run_sk(w, 0, 0, True, grid, config, orc)
