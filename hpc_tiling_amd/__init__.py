@@ -233,93 +233,116 @@ def mi_sgemm_config_count(kernel) -> int:
 # ---------------------------------------------------------------------------
 # torch tensor helpers
 # ---------------------------------------------------------------------------
-def _check_tensor(t, name):
+def _mat(t, name):
+    """(pointer, ld, transposed, rows, cols, device index) of a 2-D float32
+    device tensor stored row-major (unit column stride; ld = row stride) or
+    column-major (unit row stride, i.e. the transpose of a row-major matrix;
+    ld = column stride).  Each tensor attribute is read once: these checks
+    sit in front of every call."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32, got {t.dtype}")
-    if not t.is_cuda:
+    dev = t.get_device()
+    if dev < 0:
         raise ValueError(f"{name} must be a device tensor")
-    if t.dim() != 2:
+    shape = t.shape
+    if len(shape) != 2:
         raise ValueError(f"{name} must be 2-D")
-
-
-def _layout(t, name):
-    """(pointer, ld, transposed) of a 2-D float32 device tensor: row-major
-    (unit column stride; ld = row stride) or column-major (unit row stride,
-    i.e. the transpose of a row-major matrix; ld = column stride)."""
-    _check_tensor(t, name)
-    r, c = t.shape
-    if c <= 1 or t.stride(1) == 1:
-        ld = max(t.stride(0), c, 1) if r > 1 else max(c, 1)
-        return t.data_ptr(), ld, OP_N
-    if r <= 1 or t.stride(0) == 1:
-        ld = max(t.stride(1), r, 1) if c > 1 else max(r, 1)
-        return t.data_ptr(), ld, OP_T
+    r, c = shape
+    s0, s1 = t.stride()
+    if c <= 1 or s1 == 1:
+        ld = max(s0, c, 1) if r > 1 else max(c, 1)
+        return t.data_ptr(), ld, OP_N, r, c, dev
+    if r <= 1 or s0 == 1:
+        ld = max(s1, r, 1) if c > 1 else max(r, 1)
+        return t.data_ptr(), ld, OP_T, r, c, dev
     raise ValueError(f"{name} must be row-major or column-major (one unit stride)")
 
 
-def _operand(t, name):
-    """(pointer, ld) of a row-major operand."""
-    p, ld, trans = _layout(t, name)
-    if trans != OP_N:
-        raise ValueError(f"{name} must be row-major (unit column stride)")
-    return p, ld
-
-
-def _stream(stream, device=None):
+def _stream(stream, device):
+    """The HIP stream handle: `stream` (a torch stream or a raw handle), else
+    the current stream of device index `device`."""
     import torch
     if stream is None:
-        return torch.cuda.current_stream(device).cuda_stream
+        return torch._C._cuda_getCurrentRawStream(device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def _device_of(*tensors):
-    """The one device all given tensors (None skipped) live on.  The library
-    launches on the current device, so the helpers make this one current
-    around each call; tensors on different devices are refused."""
+    """The one device all given tensors (None skipped) live on; tensors on
+    different devices are refused."""
     devs = {t.device for t in tensors if t is not None}
     if len(devs) != 1:
         raise ValueError(f"tensors are on different devices: {sorted(str(d) for d in devs)}")
     return devs.pop()
 
 
-def _output(A, B, C, beta):
+class _Unchanged:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+_UNCHANGED = _Unchanged()
+
+
+def _current(dev):
+    """A context with device index `dev` current: the library launches on the
+    current device.  The device is switched only when it differs."""
     import torch
-    m, k = A.shape
-    k2, n = B.shape
+    if torch.cuda.current_device() == dev:
+        return _UNCHANGED
+    return torch.cuda.device(dev)
+
+
+def _same_device(dev, *tensors):
+    """Refuse tensors (None skipped) that are not on device index `dev`."""
+    for t in tensors:
+        if t is not None and t.get_device() != dev:
+            raise ValueError(f"tensors are on different devices: cuda:{dev} and {t.device}")
+
+
+def _mats(A, B, C, beta):
+    """Layouts of A (m x k), B (k x n) and C (m x n, allocated when None):
+    (A's, B's, C's (pointer, ld, transposed), m, n, k, C, device index)."""
+    import torch
+    pa, lda, ta, m, k, da = _mat(A, "A")
+    pb, ldb, tb, k2, n, db = _mat(B, "B")
     if k2 != k:
         raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
     if C is None:
         if beta != 0:
             raise ValueError("beta != 0 needs C")
         C = torch.empty((m, n), dtype=torch.float32, device=A.device)
-    if tuple(C.shape) != (m, n):
+    pc, ldc, tc, mc, nc, dc = _mat(C, "C")
+    if mc != m or nc != n:
         raise ValueError(f"C is {tuple(C.shape)}, expected {(m, n)}")
-    return m, n, k, C
+    if not da == db == dc:
+        _same_device(da, A, B, C)
+    return (pa, lda, ta), (pb, ldb, tb), (pc, ldc, tc), m, n, k, C, da
 
 
 def _prepare(A, B, C, beta):
     """Row-major A, B and C (the VALU and atomic paths)."""
-    m, n, k, C = _output(A, B, C, beta)
-    pa, lda = _operand(A, "A")
-    pb, ldb = _operand(B, "B")
-    pc, ldc = _operand(C, "C")
-    return m, n, k, pa, lda, pb, ldb, C, pc, ldc
+    a, b, c, m, n, k, C, dev = _mats(A, B, C, beta)
+    for (_, _, trans), name in ((a, "A"), (b, "B"), (c, "C")):
+        if trans != OP_N:
+            raise ValueError(f"{name} must be row-major (unit column stride)")
+    return m, n, k, a[0], a[1], b[0], b[1], C, c[0], c[1], dev
 
 
 def _prepare_ex(A, B, C, beta):
     """Operands in either storage order.  A column-major C is written as its
     row-major transpose: C^T = op(B)^T op(A)^T, i.e. the call with A and B
     swapped, each with its transpose flag flipped."""
-    m, n, k, C = _output(A, B, C, beta)
-    pa, lda, ta = _layout(A, "A")
-    pb, ldb, tb = _layout(B, "B")
-    pc, ldc, tc = _layout(C, "C")
+    (pa, lda, ta), (pb, ldb, tb), (pc, ldc, tc), m, n, k, C, dev = _mats(A, B, C, beta)
     if tc == OP_N:
-        return (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc
-    return (1 - tb, 1 - ta, n, m, k, pb, ldb, pa, lda), C, pc, ldc
+        return (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev
+    return (1 - tb, 1 - ta, n, m, k, pb, ldb, pa, lda), C, pc, ldc, dev
 
 
 def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
@@ -327,10 +350,8 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
     A (m x k), B (k x n), C (m x n): float32 device tensors, each row-major
     or column-major (a transposed view such as ``X.t()`` is passed as the
     transposed operand, without a copy)."""
-    import torch
-    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc = _prepare_ex(A, B, C, beta)
-    dev = _device_of(A, B, C)
-    with torch.cuda.device(dev):
+    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev = _prepare_ex(A, B, C, beta)
+    with _current(dev):
         s = _stream(stream, dev)
         if config is None:
             st = lib.mi_sgemm_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, s)
@@ -345,10 +366,8 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
 def sgemm_valu(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
     """Same as sgemm (row-major operands only), on the register-tiled VALU
     kernel."""
-    import torch
-    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
-    dev = _device_of(A, B, C)
-    with torch.cuda.device(dev):
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _prepare(A, B, C, beta)
+    with _current(dev):
         st = lib.mi_sgemm_valu(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
                                _stream(stream, dev))
     if st != SUCCESS:
@@ -372,13 +391,12 @@ def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, st
     """Same as sgemm with the k range split into slices; `workspace` is a
     device tensor of at least mi_sgemm_splitk_workspace_bytes bytes (allocated
     here when None).  `config` forces the partial kernel's tile configuration."""
-    import torch
-    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc = _prepare_ex(A, B, C, beta)
+    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev = _prepare_ex(A, B, C, beta)
     if workspace is None:
         workspace = splitk_workspace(m, n, k, splits, device=A.device, config=config)
-    dev = _device_of(A, B, C, workspace)
+    _same_device(dev, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
-    with torch.cuda.device(dev):
+    with _current(dev):
         s = _stream(stream, dev)
         if config is None:
             st = lib.mi_sgemm_splitk_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
@@ -403,13 +421,12 @@ def sgemm_streamk(A, B, C=None, alpha=1.0, beta=0.0, grid=0, workspace=None, str
                   config=-1):
     """Same as sgemm on a forced stream-K schedule (`grid` workgroups, 0 for
     one per resident slot of every CU); `workspace` as streamk_workspace."""
-    import torch
-    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc = _prepare_ex(A, B, C, beta)
+    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev = _prepare_ex(A, B, C, beta)
     if workspace is None:
         workspace = streamk_workspace(m, n, k, grid, device=A.device, config=config)
-    dev = _device_of(A, B, C, workspace)
+    _same_device(dev, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
-    with torch.cuda.device(dev):
+    with _current(dev):
         st = lib.mi_sgemm_streamk(config, ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc,
                                   ldc, grid, workspace.data_ptr(), ws_bytes, _stream(stream, dev))
     if st != SUCCESS:
@@ -420,10 +437,8 @@ def sgemm_streamk(A, B, C=None, alpha=1.0, beta=0.0, grid=0, workspace=None, str
 def sgemm_splitk_atomic(A, B, C=None, alpha=1.0, beta=0.0, splits=0, stream=None):
     """Split-K with atomic accumulation into C (row-major operands; no
     workspace; not bitwise reproducible run to run)."""
-    import torch
-    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _prepare(A, B, C, beta)
-    dev = _device_of(A, B, C)
-    with torch.cuda.device(dev):
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _prepare(A, B, C, beta)
+    with _current(dev):
         st = lib.mi_sgemm_splitk_atomic(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
                                         _stream(stream, dev))
     if st != SUCCESS:
@@ -446,8 +461,9 @@ def reduce_sum(x, out=None, workspace=None, stream=None):
         workspace = torch.empty(max(mi_reduce_sum_workspace_bytes(n), 4), dtype=torch.uint8,
                                 device=x.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    dev = _device_of(x, out, workspace)
-    with torch.cuda.device(dev):
+    dev = x.get_device()
+    _same_device(dev, out, workspace)
+    with _current(dev):
         st = lib.mi_reduce_sum(n, x.data_ptr() if n else None, out.data_ptr(),
                                workspace.data_ptr(), ws_bytes, _stream(stream, dev))
     if st != SUCCESS:
