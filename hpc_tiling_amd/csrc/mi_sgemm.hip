@@ -64,7 +64,7 @@ double tile_cost(int m, int n, int id, double efficiency) {
 // waves in a 4 x 2 layout) cover each other's barrier waits; on MI355X that
 // is 0.6-1.0 % faster than the 16-wave tile once the grid runs 8 or more
 // rounds of 128 x 128 tiles (8192^3, 8192^2 x 4096, 6144^3,
-// 4096 x 8192 x 8192, 12288^2 x 4096, measured back to back on one box),
+// 4096 x 8192 x 8192, 12288^2 x 4096, measured back to back on one MI355X),
 // level at four rounds and slower on one.
 constexpr int kTwoBufferId = 11;
 constexpr long long kTwoBufferMinRounds = 8;

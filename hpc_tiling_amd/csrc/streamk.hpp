@@ -27,20 +27,31 @@ __global__ __launch_bounds__(kFixupThreads) void streamk_fixup_kernel(
     int tiles_n, int group_m, int m, int n, float alpha, float beta, float *C, long long ldc) {
     const long long b = (long long)(blockIdx.x / kFixupSplit) + 1;
     const int band = blockIdx.x % kFixupSplit;
-    const long long x = sk_begin(b, iters, grid);
-    if (x >= iters || x % ksteps == 0) return;
-    const long long t = x / ksteps;
-    const long long first = sk_owner(t * ksteps, iters, grid);
+    // The index arithmetic sits in front of every block's first load: while
+    // every numerator below (at most iters * (grid + 1)) fits in 32 bits, the
+    // divisions are done in 32-bit unsigned arithmetic (same quotients, a
+    // fraction of the instructions of a 64-bit division).
+    const bool narrow = iters * (grid + 1) < (1ll << 32);
+    auto div = [narrow](long long a, long long d) -> long long {
+        return narrow ? (long long)((unsigned)a / (unsigned)d) : a / d;
+    };
+    auto begin = [&](long long w) { return div(w * iters, grid); };
+    auto owner = [&](long long x) { return div((x + 1) * grid + iters - 1, iters) - 1; };
+    const long long x = begin(b);
+    if (x >= iters) return;
+    const long long t = div(x, ksteps);
+    if (x == t * ksteps) return;
+    const long long first = owner(t * ksteps);
     if (first + 1 != b) return;
-    const long long last = sk_owner(t * ksteps + ksteps - 1, iters, grid);
+    const long long last = owner(t * ksteps + ksteps - 1);
     const int parts = (int)(last - first + 1);
 
     // slot offset of every part (-1: a workgroup with an empty range)
     __shared__ long long part_off[kFixupMaxParts];
     for (int q = threadIdx.x; q < parts; q += kFixupThreads) {
         const long long w = first + q;
-        const long long wb = sk_begin(w, iters, grid);
-        part_off[q] = sk_begin(w + 1, iters, grid) == wb
+        const long long wb = begin(w);
+        part_off[q] = begin(w + 1) == wb
                           ? -1
                           : (w * 2 + (wb > t * ksteps ? 0 : 1)) * (long long)(BM * BN);
     }
@@ -48,8 +59,9 @@ __global__ __launch_bounds__(kFixupThreads) void streamk_fixup_kernel(
 
     // Lane l of band j holds float4 groups j * BAND + l, j * BAND + l + 256,
     // ... of the tile (row-major, BN a multiple of 4).  The parts are added in
-    // order, two parts' loads in flight together.  Entries of the slots
-    // outside C's extent were never written and are not stored.
+    // order, the loads of PG parts in flight together (a tile is usually
+    // shared by two or three workgroups: one round trip to memory).  Entries
+    // of the slots outside C's extent were never written and are not stored.
     constexpr int BAND = BM * BN / 4 / kFixupSplit;
     constexpr int PER = BAND / kFixupThreads;
     static_assert(PER >= 1 && BAND % kFixupThreads == 0, "a band must fill the block");
@@ -61,34 +73,44 @@ __global__ __launch_bounds__(kFixupThreads) void streamk_fixup_kernel(
     f32x4 acc[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    int q = 0;
-    for (; q + 1 < parts; q += 2) {
-        const long long o0 = part_off[q], o1 = part_off[q + 1];
-        f32x4 v0[PER], v1[PER];
+    // Positions past the last part add +0, which leaves every sum unchanged
+    // (a sum that starts at +0 is never -0).
+    constexpr int PG = 4;
+    for (int q = 0; q < parts; q += PG) {
+        f32x4 v[PG][PER];
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            v0[u] = part(o0, u);
-            v1[u] = part(o1, u);
+        for (int i = 0; i < PG; ++i) {
+            const long long o = q + i < parts ? part_off[q + i] : -1;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) v[i][u] = part(o, u);
         }
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            acc[u] += v0[u];
-            acc[u] += v1[u];
-        }
-    }
-    if (q < parts) {
-        const long long o0 = part_off[q];
+        for (int i = 0; i < PG; ++i)
 #pragma unroll
-        for (int u = 0; u < PER; ++u) acc[u] += part(o0, u);
+            for (int u = 0; u < PER; ++u) acc[u] += v[i][u];
     }
     int tm, tn;
     grouped_tile(tile0 + (int)t, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    // Columns come in groups of four from a multiple of 4, so with C 16-byte
+    // aligned and ldc a multiple of 4 a whole group is one 16-byte access.
+    const bool vec = (reinterpret_cast<unsigned long long>(C) & 15) == 0 && ldc % 4 == 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int e = 4 * (g0 + u * kFixupThreads);
         const int row = m0 + e / BN, col = n0 + e % BN;
         if (row >= m) continue;
+        if (vec && col + 3 < n) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(C + (long long)row * ldc + col);
+            f32x4 v = alpha * acc[u];
+            if (beta != 0.f) {
+                const f32x4 c = *dst;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = __builtin_fmaf(beta, c[j], v[j]);
+            }
+            *dst = v;
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (col + j >= n) break;
