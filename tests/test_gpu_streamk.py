@@ -136,3 +136,30 @@ def test_streamk_k_sweep(orc, config):
         w = synth.Workload(10, "skk", 150, 140, k, k + 4, 144, 141, "uniform", "int3", 1.0, 0.5)
         for grid in (3, 7):
             run_sk(w, 0, 0, True, grid, config, orc)
+
+
+# The fixup writes C in 16-byte groups only when C is 16-byte aligned and ldc
+# is a multiple of 4.  A C that starts 1-3 floats past an aligned address
+# (ldc 132, a multiple of 4) must take the element-wise stores, as must
+# ldc 133; column 128 of n = 129 is a partial group at the right edge.
+# Grid 37 over 4 tiles of 10 k steps shares every tile among 9-10
+# workgroups, so the fixup adds parts in several groups of loads.
+@pytest.mark.parametrize("off", [0, 1, 2, 3])
+@pytest.mark.parametrize("ldc", [132, 133])
+def test_streamk_c_alignment(orc, off, ldc):
+    w = synth.Workload(11, "skalign", 130, 129, 300, 304, 132, ldc, "uniform", "int3", 1.0, 0.5)
+    A, lda, B, ldb, C = synth.operands_ex(w, 0, 0, integer_twin=True)
+    say("streamk C offset", off, "ldc", ldc)
+    flat = torch.full((off + C.size + 8,), float("nan"), device="cuda")
+    flat[off:off + C.size] = torch.from_numpy(C.reshape(-1)).cuda()
+    Cv = torch.as_strided(flat, (w.m, w.n), (ldc, 1), off)
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    hta.sgemm_streamk(Ad[:, :w.k], Bd[:, :w.n], Cv, w.alpha, w.beta, grid=37, config=9)
+    torch.cuda.synchronize()
+    got = flat.cpu().numpy()
+    assert np.isnan(got[:off]).all() and np.isnan(got[off + C.size:]).all(), "wrote outside C"
+    out = got[off:off + C.size].reshape(w.m, ldc)
+    assert np.array_equal(out[:, w.n:], C[:, w.n:]), "C padding written"
+    ref = orc.sgemm(w.m, w.n, w.k, w.alpha, A, lda, B, ldb, w.beta, C, ldc)
+    assert_exact(out[:, :w.n], ref["C"].reshape(w.m, ldc)[:, :w.n],
+                 f"streamk C offset {off} ldc {ldc}")
