@@ -3,6 +3,7 @@
 // include/mi_sgemm.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cstdint>
@@ -321,11 +322,19 @@ bool vector_ok(const float *A, int lda, const float *B, int ldb) {
     return aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0;
 }
 
+// A dispatch describes its grid in work-items with 32 bits: launches beyond
+// that are refused.  Only a C of about 2^36 elements and more, or a forced
+// slice count of that order, comes near it; multi-kernel paths check their
+// first large launch before anything is enqueued, so a refusal writes nothing.
+bool launch_fits(long long grid, int threads) {
+    return grid <= INT_MAX && grid * threads <= (long long)UINT32_MAX;
+}
+
 // Every launch reports the status hipLaunchKernel itself returns (not a
 // sticky error another library may have left behind).
 int launch_raw(const void *fn, long long grid, int threads, void **args, hipStream_t stream) {
     if (grid <= 0) return MI_SGEMM_SUCCESS;
-    if (grid > INT_MAX) return MI_SGEMM_ERROR_INVALID_VALUE;
+    if (!launch_fits(grid, threads)) return MI_SGEMM_ERROR_INVALID_VALUE;
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), args, 0, stream) == hipSuccess
                ? MI_SGEMM_SUCCESS
                : MI_SGEMM_ERROR_LAUNCH;
@@ -474,7 +483,9 @@ int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, con
     st = launch(c.split[ta][tb][vector_ok(A, lda, B, ldb)], grid, 64 * c.wgm * c.wgn, s, a);
     if (st) return st;
 
-    const long long blocks = ceil_div(ceil_div((long long)m * n, 64), 4);
+    // (the combine walks its chunks grid-stride, so the block count is capped)
+    const long long blocks =
+        std::min(ceil_div(ceil_div((long long)m * n, 64), 4), kCombineMaxBlocks);
     const float *wsc = wsa;
     long long slice = sp.slice, ldc64 = ldc;
     int nsplit = sp.splits;
@@ -501,17 +512,20 @@ int run_splitk_atomic(int config, int m, int n, int k, float alpha, const float 
     const SplitPlan sp = plan_split(m, n, k, splits, config, false);  // slices only
     const int id = sp.config;
     if (sp.splits == 1) return launch_full(id, 0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s);
-    if (beta != 1.f) {
-        st = launch_scale(m, n, beta, C, ldc, s);
-        if (st) return st;
-    }
     const MfmaConfig &c = mfma_config(id);
     GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
     a.tiles_m = (int)ceil_div(m, c.bm);
     a.tiles_n = (int)ceil_div(n, c.bn);
     a.k_per_split = sp.k_per_split;
     const long long grid = (long long)a.tiles_m * a.tiles_n * sp.splits;
-    return launch(c.atomic[vector_ok(A, lda, B, ldb)], grid, 64 * c.wgm * c.wgn, s, a);
+    const int threads = 64 * c.wgm * c.wgn;
+    // checked before C is scaled, so that a refused launch leaves C as it was
+    if (!launch_fits(grid, threads)) return MI_SGEMM_ERROR_INVALID_VALUE;
+    if (beta != 1.f) {
+        st = launch_scale(m, n, beta, C, ldc, s);
+        if (st) return st;
+    }
+    return launch(c.atomic[vector_ok(A, lda, B, ldb)], grid, threads, s, a);
 }
 
 // Stream-K with a forced grid (0: automatic) and configuration (< 0: the

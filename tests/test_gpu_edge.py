@@ -201,3 +201,52 @@ def test_concurrent_host_threads_and_streams():
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
     assert not errors, errors
+
+
+def test_launch_beyond_32bit_work_items_refused():
+    """A dispatch holds its grid size in work-items as 32 bits.  Atomic
+    split-K at 16384^2 x 32768 with 1024 forced slices plans 2^24 workgroups
+    of 256 lanes, i.e. 2^32 work-items: the call is refused with
+    INVALID_VALUE before C is scaled, and C keeps its values.  (The operands
+    are real buffers of the full size, so a launch could only compute.)"""
+    m = n = 16384
+    k, splits = 32768, 1024
+    plan = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK_ATOMIC, -1, m, n, k, splits)
+    assert plan["workgroups"] * plan["threads"] > 2**32 - 1
+    say("refused launch", m, n, k, splits, plan["workgroups"], plan["threads"])
+    A = torch.zeros((m, k), device="cuda")
+    B = torch.zeros((k, n), device="cuda")
+    C = torch.full((m, n), 7.0, device="cuda")
+    st = hta.mi_sgemm_splitk_atomic(m, n, k, 1.0, A.data_ptr(), k, B.data_ptr(), n, 0.5,
+                                    C.data_ptr(), n, splits)
+    torch.cuda.synchronize()
+    assert st == hta.ERROR_INVALID_VALUE
+    assert bool((C == 7.0).all())
+    del A, B, C
+    torch.cuda.empty_cache()
+
+
+def test_splitk_combine_past_its_block_cap():
+    """The combine kernel caps its grid at 2^20 blocks of four waves and walks
+    the rest of the 64-output chunks grid-stride: 16384 x 16400 has 1049600
+    blocks' worth, so the last 1024 blocks' chunks (the last rows of C) are
+    done on a second pass.  Integer operands: every element equals the
+    single-pass result, and sampled rows (the last 16 among them) equal the
+    exact integer product."""
+    rng = np.random.default_rng(12)
+    m, n, k = 16384, 16400, 64
+    plan = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, m, n, k, 2)
+    assert plan["splits"] == 2 and plan["stream_k_grid"] == 0
+    say("combine past cap", m, n, k)
+    Ah, Bh = ints(rng, (m, k)), ints(rng, (k, n))
+    A, B = torch.from_numpy(Ah).cuda(), torch.from_numpy(Bh).cuda()
+    C = torch.empty((m, n), device="cuda")
+    hta.sgemm_splitk(A, B, C, splits=2)
+    C1 = hta.sgemm(A, B)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C1)
+    rows = np.concatenate([np.arange(0, m, 997), np.arange(m - 16, m)])
+    got = C[torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert_exact(got, exact_product(Ah[rows], Bh), "combine past its block cap")
+    del A, B, C, C1
+    torch.cuda.empty_cache()
