@@ -56,7 +56,11 @@ typedef enum mi_status {
     MI_SGEMM_SUCCESS = 0,
     MI_SGEMM_ERROR_INVALID_VALUE = 1, /* m, n or k < 0; splits < 0 or > k; a transpose
                                          flag other than 0 or 1; unknown kernel or
-                                         config id; grid too large */
+                                         config id; a launch of 2^31 or more
+                                         workgroups or 2^32 or more work-items
+                                         (a C of about 2^36 elements, or a forced
+                                         slice count of that order); refused
+                                         before anything is enqueued */
     MI_SGEMM_ERROR_INVALID_LD = 2,    /* lda < max(1,k), ldb < max(1,n) or ldc < max(1,n)
                                          (m for lda, k for ldb when transposed) */
     MI_SGEMM_ERROR_NULL_POINTER = 3,  /* NULL for an operand that would be read or written */
