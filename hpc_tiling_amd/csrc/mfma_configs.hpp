@@ -63,7 +63,8 @@ template <> struct TileOf<5> { using type = MfmaTile<128, 256, 16, 2, 4>; };
 template <> struct TileOf<6> { using type = MfmaTile<64, 64, 32, 2, 2>; };
 template <> struct TileOf<7> { using type = MfmaTile<256, 128, 32, 2, 4>; };
 template <> struct TileOf<8> { using type = MfmaTile<128, 64, 32, 2, 2>; };
-template <> struct TileOf<9> { using type = MfmaTile<128, 128, 32, 4, 4>; };
+// 16 waves, one workgroup per CU: a four-buffer ring (128 KB of LDS)
+template <> struct TileOf<9> { using type = MfmaTile<128, 128, 32, 4, 4, 4>; };
 // two-buffer rings, two workgroups per CU
 template <> struct TileOf<10> { using type = MfmaTile<128, 128, 16, 2, 4, 2>; };
 template <> struct TileOf<11> { using type = MfmaTile<128, 128, 32, 4, 2, 2>; };

@@ -5,12 +5,12 @@
 //   * a workgroup of WGM x WGN waves owns a BM x BN tile of C and walks k in
 //     steps of BK ("big iterations");
 //   * each step stages a BM x BK tile of A and a BK x BN tile of B in a ring
-//     of three LDS buffers (two for tiles built for two workgroups per CU).
-//     Whole k steps use gfx950's direct global->LDS loads
-//     (buffer_load_dwordx4 ... lds, 16 bytes per lane, for aligned operands;
-//     buffer_load_dword ... lds, 4 bytes per lane, otherwise; no VGPRs
-//     involved), issued two steps ahead (one with two buffers); the partial
-//     last k step (and
+//     of three LDS buffers (two for tiles built for two workgroups per CU,
+//     four for the 16-wave 128 x 128 x 32 tile).  Whole k steps use gfx950's
+//     direct global->LDS loads (buffer_load_dwordx4 ... lds, 16 bytes per
+//     lane, for aligned operands; buffer_load_dword ... lds, 4 bytes per
+//     lane, otherwise; no VGPRs involved), issued one step ahead per buffer
+//     beyond the first; the partial last k step (and
 //     tiles whose byte offsets exceed the buffer range) use masked 16-byte
 //     or element loads through VGPRs with out-of-range elements stored as
 //     zeros (page aerisun.top, section "Shared Tiling 与 block 内复用");
@@ -59,7 +59,7 @@ template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int STAGES_ = 3,
           int WGS_ = (STAGES_ == 2 ? 2 : 1)>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
-    static constexpr int STAGES = STAGES_;                // LDS buffers in the ring (2 or 3)
+    static constexpr int STAGES = STAGES_;                // LDS buffers in the ring (2 to 4)
     static constexpr int DIST = STAGES - 1;               // steps a load runs ahead
     static constexpr int WAVES = WGM * WGN;
     static constexpr int NT = 64 * WAVES;
@@ -75,7 +75,7 @@ struct MfmaTile {
     static_assert(GROUPS % 2 == 0, "fragment double-buffering needs an even group count");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
-    static_assert(STAGES == 2 || STAGES == 3, "ring of two or three buffers");
+    static_assert(STAGES >= 2 && STAGES <= 4, "ring of two to four buffers");
 };
 
 // Four floats of an e-contiguous fragment (read one by one).
@@ -210,6 +210,23 @@ __device__ __forceinline__ void load_lds4(const float *base, float *lds, int vof
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_ptr(lds), 4, voffset, 0, 0, 0);
 }
 
+// The barrier at the end of a step of a four-buffer ring: this wave's LDS
+// reads and all but its newest N vector-memory operations (the direct loads
+// just issued, for the step three ahead) complete, then the workgroup meets.
+// s_waitcnt fields on gfx9-class parts: vmcnt in bits 3:0 and 15:14, expcnt
+// in bits 6:4 (7: no wait), lgkmcnt in bits 11:8.  The empty asm statements
+// keep the compiler from moving memory accesses across the wait or the
+// barrier (the barrier intrinsic alone does not order them).
+template <int N>
+__device__ __forceinline__ void barrier_keep_newest() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    constexpr int kImm = (N & 15) | ((N >> 4) << 14) | (7 << 4);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kImm);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // What a step loads for the step DIST ahead (see one_step in the kernel).
 constexpr int kLoadNone = 0, kLoadDirect = 1, kLoadRegs = 2, kLoadAuto = 3;
 
@@ -237,6 +254,12 @@ constexpr int kLoadNone = 0, kLoadDirect = 1, kLoadRegs = 2, kLoadAuto = 3;
 // loads one step ahead instead: buffer (t+1) % 2 was read during step t-1,
 // and step t+1's first fragments are read after the barrier of step t; the
 // other workgroup resident on the CU keeps the matrix cores busy meanwhile.
+// A four-buffer ring loads three steps ahead, into buffer (t+3) % 4 (read
+// during step t-1), behind the first MFMA group of step t, and its barrier
+// waits only for the loads issued a step earlier: every load has nearly two
+// steps to land instead of one (the three-buffer barrier waits for all of
+// them), and the loads' issue no longer holds back the first MFMAs after the
+// barrier.
 template <class T, bool VEC, int MODE, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::WAVES_PER_SIMD)))
 void sgemm_mfma_kernel(GemmArgs p) {
@@ -249,20 +272,24 @@ void sgemm_mfma_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(1024))) float As0[OA::ELEMS];
     __shared__ __attribute__((aligned(1024))) float As1[OA::ELEMS];
     __shared__ __attribute__((aligned(1024))) float As2[T::STAGES > 2 ? OA::ELEMS : 4];
+    __shared__ __attribute__((aligned(1024))) float As3[T::STAGES > 3 ? OA::ELEMS : 4];
     __shared__ __attribute__((aligned(1024))) float Bs0[OB::ELEMS];
     __shared__ __attribute__((aligned(1024))) float Bs1[OB::ELEMS];
     __shared__ __attribute__((aligned(1024))) float Bs2[T::STAGES > 2 ? OB::ELEMS : 4];
+    __shared__ __attribute__((aligned(1024))) float Bs3[T::STAGES > 3 ? OB::ELEMS : 4];
     auto a_buf = [&](auto s) -> float * {
         constexpr int S = decltype(s)::value;
         if constexpr (S == 0) return As0;
         else if constexpr (S == 1) return As1;
-        else return As2;
+        else if constexpr (S == 2) return As2;
+        else return As3;
     };
     auto b_buf = [&](auto s) -> float * {
         constexpr int S = decltype(s)::value;
         if constexpr (S == 0) return Bs0;
         else if constexpr (S == 1) return Bs1;
-        else return Bs2;
+        else if constexpr (S == 2) return Bs2;
+        else return Bs3;
     };
 
     const int tid = threadIdx.x;
@@ -443,10 +470,27 @@ void sgemm_mfma_kernel(GemmArgs p) {
                 store_regs(st, buf);
             }
         };
-        constexpr int NS = T::STAGES, D = T::DIST;
+        // Stream-K runs a four-buffer tile as a three-buffer ring: its
+        // segments restart the pipeline mid-kernel, and the deeper ring
+        // measured slower there.
+        constexpr int NS = MODE == kStreamK && T::STAGES > 3 ? 3 : T::STAGES, D = NS - 1;
+        // direct loads one wave issues per step
+        constexpr int DIRECT_LOADS = VEC ? OA::PER + OB::PER : OA::PER4 + OB::PER4;
         fill(0, S0{});
-        if (D == 2 && nsteps > 1) fill(1, S1{});
-        __syncthreads();
+        if (D >= 2 && nsteps > 1) fill(1, S1{});
+        if (D >= 3 && nsteps > 2) fill(2, std::integral_constant<int, 2>{});
+        // Four buffers: the first two tiles must be resident (step 0 reads
+        // step 1's first fragments before its barrier); the third may still
+        // be on its way, if it was loaded directly.
+        if (D >= 3 && 2 < ndirect)
+            barrier_keep_newest<DIRECT_LOADS>();
+        else
+            __syncthreads();
+        // Group of a step before which its direct loads are issued: with four
+        // buffers a load has nearly two steps to land, and issued behind the
+        // first MFMA group it no longer delays that group after the barrier.
+        constexpr int LOAD_GROUP = NS == 4 ? 1 : 0;
+        static_assert(LOAD_GROUP < T::GROUPS, "the loads must be issued in the step");
         read_frag(f[0], S0{}, 0);
 
         // One step with its ring position CUR = step % NS fixed at compile
@@ -466,20 +510,22 @@ void sgemm_mfma_kernel(GemmArgs p) {
             const bool ahead = LOAD == kLoadAuto ? step + D < nsteps : LOAD != kLoadNone;
             const bool direct = LOAD == kLoadAuto ? step + D < ndirect : LOAD == kLoadDirect;
             Stage st;
-            if (direct)
-                load_direct(step + D, WRT{});
-            else if (ahead)
-                load_regs(st, step + D);
+            if (!direct && ahead) load_regs(st, step + D);
+            if (LOAD_GROUP == 0 && direct) load_direct(step + D, WRT{});
             // The fences keep the scheduler from sinking the loads and the
             // next group's LDS reads below the MFMAs that hide them.
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int g = 0; g < T::GROUPS; ++g) {
+                if (g > 0 && g == LOAD_GROUP && direct) {
+                    load_direct(step + D, WRT{});
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 // (the last step reads the next buffer too: stale, unused, and
                 // without a branch in front of the last MFMA group)
                 if (g + 1 < T::GROUPS) {
                     read_frag(f[(g + 1) & 1], cur, g + 1);
-                } else if (D == 2) {
+                } else if (D >= 2) {
                     read_frag(f[0], NXT{}, 0);  // GROUPS is even: step+1 starts on set 0
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -487,11 +533,18 @@ void sgemm_mfma_kernel(GemmArgs p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (!direct && ahead) store_regs(st, WRT{});
-            __syncthreads();
+            // Four buffers: the loads just issued (for step + 3) keep running
+            // across the barrier; the ones issued a step earlier (step + 2)
+            // must be complete, in every wave, before it.
+            if (NS == 4 && direct)
+                barrier_keep_newest<DIRECT_LOADS>();
+            else
+                __syncthreads();
             // two buffers: step + 1's tile is complete only after the barrier
             if (D == 1) read_frag(f[0], NXT{}, 0);
         };
         using S2 = std::integral_constant<int, 2>;
+        using S3 = std::integral_constant<int, 3>;
         using LD = std::integral_constant<int, kLoadDirect>;
         using LA = std::integral_constant<int, kLoadAuto>;
         int step = 0;
@@ -502,6 +555,7 @@ void sgemm_mfma_kernel(GemmArgs p) {
             one_step(step, LD{}, S0{});
             one_step(step + 1, LD{}, S1{});
             if constexpr (NS > 2) one_step(step + 2, LD{}, S2{});
+            if constexpr (NS > 3) one_step(step + 3, LD{}, S3{});
         }
         // Without direct loads (huge leading dimensions) whole rounds of the
         // ring go through the deciding step too, so step % NS stays 0.
@@ -509,6 +563,7 @@ void sgemm_mfma_kernel(GemmArgs p) {
             one_step(step, LA{}, S0{});
             one_step(step + 1, LA{}, S1{});
             if constexpr (NS > 2) one_step(step + 2, LA{}, S2{});
+            if constexpr (NS > 3) one_step(step + 3, LA{}, S3{});
         }
         // The last R <= 5 steps (step % NS == 0 here), ND of them whole k
         // steps, as one of a few sequences fixed at compile time: step i
