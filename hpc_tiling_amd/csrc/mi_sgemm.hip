@@ -24,7 +24,7 @@ namespace {
 const MfmaConfig *const kMfmaConfigTable[kNumMfmaConfigs] = {
     &kMfmaConfig0, &kMfmaConfig1, &kMfmaConfig2, &kMfmaConfig3, &kMfmaConfig4, &kMfmaConfig5,
     &kMfmaConfig6, &kMfmaConfig7, &kMfmaConfig8, &kMfmaConfig9, &kMfmaConfig10, &kMfmaConfig11,
-    &kMfmaConfig12,
+    &kMfmaConfig12, &kMfmaConfig13,
 };
 const MfmaConfig &mfma_config(int id) { return *kMfmaConfigTable[id]; }
 
@@ -79,8 +79,16 @@ constexpr long long kTwoBufferMinRounds = 8;
 constexpr int kSmallStepId = 12;
 constexpr long long kSmallStepMinRounds = 8;
 
+// The same tile with a four-buffer ring (id 13, five workgroups per CU; a
+// load then has nearly two k steps to land) wins once k is long enough to
+// pay for the deeper prologue: over k = 257 .. 4095 at 3000 x 5000,
+// 2500 x 6000 and 8000^2 it lost 1-4 % up to k = 777 and won 0.5-2 % from
+// k = 900 on (3000 x 5000 x 1023: 123.5 -> 125.0, x 2047: 127.9 -> 130.5;
+// forced configurations, back to back on one MI355X).
+constexpr int kSmallStepDeepId = 13;
+constexpr int kSmallStepDeepMinK = 848;
+
 int choose_mfma_config(int m, int n, int k) {
-    (void)k;
     int best = kCandidates[0].id;
     double best_cost = tile_cost(m, n, best, kCandidates[0].efficiency);
     for (const Candidate &cand : kCandidates) {
@@ -93,7 +101,7 @@ int choose_mfma_config(int m, int n, int k) {
     if (best == 9 && tile_count(m, n, kTwoBufferId) >= kTwoBufferMinRounds * kCUs)
         best = kTwoBufferId;
     if (best == 6 && k % 32 != 0 && tile_count(m, n, kSmallStepId) >= kSmallStepMinRounds * kCUs)
-        best = kSmallStepId;
+        best = k >= kSmallStepDeepMinK ? kSmallStepDeepId : kSmallStepId;
     return best;
 }
 

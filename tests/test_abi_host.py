@@ -258,7 +258,8 @@ def test_tile_choice_rules():
     one to seven rounds, the two-buffer 128 x 128 x 32 tile from 8 rounds of
     128 x 128 tiles, 64 x 64 x 32 where it quantises better, and 64 x 64 x 16
     (six workgroups per CU) when k leaves a partial 32-wide step on 8 or more
-    rounds of 64 x 64 tiles."""
+    rounds of 64 x 64 tiles, in its four-buffer form (five per CU) from
+    k = 848 on."""
     def tile(m, n, k):
         p = hta.mi_sgemm_get_plan(hta.KERNEL_MFMA, -1, m, n, k, 0)
         return p["tile_m"], p["tile_n"], p["tile_k"], p["threads"]
@@ -270,6 +271,10 @@ def test_tile_choice_rules():
     assert tile(3001, 4997, 1023) == (64, 64, 16, 256)         # partial k step, 3713 tiles
     assert tile(3001, 4997, 1024) == (64, 64, 32, 256)         # whole k steps
     assert tile(1000, 1000, 1000) == (64, 64, 32, 256)         # short grid
+    config = lambda m, n, k: hta.mi_sgemm_get_plan(hta.KERNEL_MFMA, -1, m, n, k, 0)["config"]
+    assert config(3001, 4997, 1023) == 13                      # four buffers, long k
+    assert config(2500, 6000, 847) == 12 and config(2500, 6000, 849) == 13
+    assert config(2500, 6000, 777) == 12                       # three buffers, short k
     # the split-K entry's single-slice plans use the same choice
     p = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, 8192, 8192, 8192, 0)
     assert p["splits"] == 1 and (p["tile_m"], p["tile_k"], p["threads"]) == (128, 32, 512)
