@@ -72,12 +72,14 @@ template <> struct TileOf<11> { using type = MfmaTile<128, 128, 32, 4, 2, 2>; };
 template <> struct TileOf<12> { using type = MfmaTile<64, 64, 16, 2, 2, 3, 6>; };
 // the same tile with a four-buffer ring, five workgroups per CU
 template <> struct TileOf<13> { using type = MfmaTile<64, 64, 16, 2, 2, 4, 5>; };
-constexpr int kNumMfmaConfigs = 14;
+// 8 waves, two workgroups per CU, a four-buffer ring (64 KB of LDS each)
+template <> struct TileOf<14> { using type = MfmaTile<128, 128, 16, 4, 2, 4, 2>; };
+constexpr int kNumMfmaConfigs = 15;
 
 // One table per configuration, each defined (constant-initialised) in its
 // own build of mfma_cfg.hip.
 extern const MfmaConfig kMfmaConfig0, kMfmaConfig1, kMfmaConfig2, kMfmaConfig3, kMfmaConfig4,
     kMfmaConfig5, kMfmaConfig6, kMfmaConfig7, kMfmaConfig8, kMfmaConfig9, kMfmaConfig10,
-    kMfmaConfig11, kMfmaConfig12, kMfmaConfig13;
+    kMfmaConfig11, kMfmaConfig12, kMfmaConfig13, kMfmaConfig14;
 
 }  // namespace mi

@@ -24,7 +24,7 @@ namespace {
 const MfmaConfig *const kMfmaConfigTable[kNumMfmaConfigs] = {
     &kMfmaConfig0, &kMfmaConfig1, &kMfmaConfig2, &kMfmaConfig3, &kMfmaConfig4, &kMfmaConfig5,
     &kMfmaConfig6, &kMfmaConfig7, &kMfmaConfig8, &kMfmaConfig9, &kMfmaConfig10, &kMfmaConfig11,
-    &kMfmaConfig12, &kMfmaConfig13,
+    &kMfmaConfig12, &kMfmaConfig13, &kMfmaConfig14,
 };
 const MfmaConfig &mfma_config(int id) { return *kMfmaConfigTable[id]; }
 
@@ -61,14 +61,16 @@ double tile_cost(int m, int n, int id, double efficiency) {
     return (double)per_cu * c.bm * c.bn / efficiency;
 }
 
-// Two resident workgroups of a two-buffer 128 x 128 x 32 tile (id 11, 8
-// waves in a 4 x 2 layout) cover each other's barrier waits; on MI355X that
-// is 0.6-1.0 % faster than the 16-wave tile once the grid runs 8 or more
-// rounds of 128 x 128 tiles (8192^3, 8192^2 x 4096, 6144^3,
-// 4096 x 8192 x 8192, 12288^2 x 4096, measured back to back on one MI355X),
-// level at four rounds and slower on one.
-constexpr int kTwoBufferId = 11;
-constexpr long long kTwoBufferMinRounds = 8;
+// Two resident workgroups of an 8-wave 128 x 128 x 16 tile (id 14, 4 x 2
+// waves, a four-buffer ring in 64 KB of LDS each) cover each other's barrier
+// waits.  Forced against the 16-wave tile and against the earlier two-buffer
+// 128 x 128 x 32 tile (id 11), back to back on one MI355X, it won from three
+// rounds of 128 x 128 tiles on: 4096^3 148.9 -> 149.7, 8192^3 151.9 ->
+// 152.5 (id 11), 8192^2 x 2048 146.4 -> 148.1 (id 11), 3072 x 4096^2 149.0
+// -> 149.5.  It was mixed at two rounds and lost at one (2048^3 145.2 ->
+// 143.1: half of the two-per-CU slots stay empty).
+constexpr int kTwoWorkgroupId = 14;
+constexpr long long kTwoWorkgroupMinRounds = 3;
 
 // When k leaves a partial 32-wide step, the 64 x 64 x 16 tile built for six
 // workgroups per CU (id 12) beats the 64 x 64 x 32 one on grids of 8 or more
@@ -98,8 +100,8 @@ int choose_mfma_config(int m, int n, int k) {
             best_cost = cost;
         }
     }
-    if (best == 9 && tile_count(m, n, kTwoBufferId) >= kTwoBufferMinRounds * kCUs)
-        best = kTwoBufferId;
+    if (best == 9 && tile_count(m, n, kTwoWorkgroupId) >= kTwoWorkgroupMinRounds * kCUs)
+        best = kTwoWorkgroupId;
     if (best == 6 && k % 32 != 0 && tile_count(m, n, kSmallStepId) >= kSmallStepMinRounds * kCUs)
         best = k >= kSmallStepDeepMinK ? kSmallStepDeepId : kSmallStepId;
     return best;

@@ -255,18 +255,20 @@ def test_streamk_argument_errors_and_plan():
 
 def test_tile_choice_rules():
     """The automatic tile choice: the 16-wave 128 x 128 x 32 tile on grids of
-    one to seven rounds, the two-buffer 128 x 128 x 32 tile from 8 rounds of
-    128 x 128 tiles, 64 x 64 x 32 where it quantises better, and 64 x 64 x 16
+    one or two rounds, the 8-wave 128 x 128 x 16 tile for two workgroups per
+    CU from 3 rounds of 128 x 128 tiles, 64 x 64 x 32 where it quantises better, and 64 x 64 x 16
     (six workgroups per CU) when k leaves a partial 32-wide step on 8 or more
     rounds of 64 x 64 tiles, in its four-buffer form (five per CU) from
     k = 848 on."""
     def tile(m, n, k):
         p = hta.mi_sgemm_get_plan(hta.KERNEL_MFMA, -1, m, n, k, 0)
         return p["tile_m"], p["tile_n"], p["tile_k"], p["threads"]
-    assert tile(2048, 2048, 2048) == (128, 128, 32, 1024)
-    assert tile(4096, 4096, 4096) == (128, 128, 32, 1024)
-    assert tile(8192, 8192, 8192) == (128, 128, 32, 512)       # two-buffer, 4 x 2 waves
-    assert tile(12288, 12288, 4096) == (128, 128, 32, 512)
+    assert tile(2048, 2048, 2048) == (128, 128, 32, 1024)      # one round of 128 x 128
+    assert tile(2048, 4096, 2048) == (128, 128, 32, 1024)      # two rounds
+    assert tile(3072, 4096, 4096) == (128, 128, 16, 512)       # three: two per CU, 4 x 2 waves
+    assert tile(4096, 4096, 4096) == (128, 128, 16, 512)
+    assert tile(8192, 8192, 8192) == (128, 128, 16, 512)
+    assert tile(12288, 12288, 4096) == (128, 128, 16, 512)
     assert tile(3072, 3072, 3072) == (64, 64, 32, 256)
     assert tile(3001, 4997, 1023) == (64, 64, 16, 256)         # partial k step, 3713 tiles
     assert tile(3001, 4997, 1024) == (64, 64, 32, 256)         # whole k steps
@@ -277,4 +279,4 @@ def test_tile_choice_rules():
     assert config(2500, 6000, 777) == 12                       # three buffers, short k
     # the split-K entry's single-slice plans use the same choice
     p = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, 8192, 8192, 8192, 0)
-    assert p["splits"] == 1 and (p["tile_m"], p["tile_k"], p["threads"]) == (128, 32, 512)
+    assert p["splits"] == 1 and (p["tile_m"], p["tile_k"], p["threads"]) == (128, 16, 512)
