@@ -460,7 +460,7 @@ void sgemm_mfma_kernel(GemmArgs p) {
     if (nsteps > 0) {
         set_frag_addr();
         Frag f[2];
-        // make the tiles of steps 0 and 1 resident
+        // load the tile of one of the first D steps
         auto fill = [&](int step, auto buf) {
             if (step < ndirect) {
                 load_direct(step, buf);
