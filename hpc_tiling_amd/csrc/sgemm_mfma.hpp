@@ -603,10 +603,15 @@ void sgemm_mfma_kernel(GemmArgs p) {
         using I4 = std::integral_constant<int, 4>;
         using I5 = std::integral_constant<int, 5>;
         const int rem = nsteps - step, nd = ndirect - step;
-        // (rem, nd): nd is rem or rem - 1 when direct loads are used, and at
-        // most 2 * NS - 2 after the steady loop.  Two-buffer rings (long k
-        // steps per tile, registers to the limit) keep the run-time tail.
+        // (rem, nd): nd is rem or rem - 1 when direct loads are used.  Without
+        // them (ndirect == 0: offsets beyond the buffer range) nd is -step,
+        // which must not reach the switch: its key would alias another
+        // (steps, whole steps) pair, running too few steps and issuing
+        // direct loads.  Two-buffer rings (long k steps per tile, registers
+        // to the limit) keep the run-time tail.
         if constexpr (NS == 2) {
+            tail_auto();
+        } else if (nd != rem && nd != rem - 1) {
             tail_auto();
         } else switch (rem * 8 + nd) {
             case 1 * 8 + 0: tail(I1{}, I0{}); break;

@@ -78,6 +78,53 @@ def test_leading_dimension_beyond_direct_load_range(which):
     torch.cuda.empty_cache()
 
 
+# k values whose step counts (9, 10, 18, 19, 28 and 37 steps of 16 or 32)
+# once made the last steps of a tile alias another compile-time tail when
+# direct loads are off, so that steps were skipped.
+HUGE_LDA_K = (140, 155, 270, 285, 300, 445, 570, 590, 600, 890, 1180)
+
+
+@pytest.mark.parametrize("config", [0, 6, 9, 12, 13, 14])
+def test_long_k_without_direct_loads(config):
+    """lda = 9e6 floats puts a tile step of A past the 2^31-byte range of a
+    direct load for every tile height used (64 and 128 rows), so every step
+    loads through VGPRs, decided at run time, and the last steps take the
+    run-time tail.  Three-buffer (0, 6, 12) and four-buffer (9, 13, 14)
+    rings, over k values with many step counts, bit-exact on integers."""
+    rng = np.random.default_rng(4)
+    m, n, kmax = 5, 70, max(HUGE_LDA_K)
+    Ah, Bh = ints(rng, (m, kmax)), ints(rng, (kmax, n))
+    A_all = padded_device(Ah, 9_000_000)
+    B_all = torch.from_numpy(Bh).cuda()
+    for k in HUGE_LDA_K:
+        say("huge lda, config", config, "k", k)
+        C = hta.sgemm(A_all[:, :k], B_all[:k], config=config)
+        torch.cuda.synchronize()
+        assert_exact(C.cpu().numpy(), exact_product(Ah[:, :k], Bh[:k]),
+                     f"huge lda, config {config}, k {k}")
+    del A_all, B_all
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("config", [6, 9, 14])
+def test_streamk_long_k_without_direct_loads(config):
+    """The same operands through a forced stream-K schedule of 3 workgroups:
+    every segment's step count goes through the same tail dispatch."""
+    rng = np.random.default_rng(5)
+    m, n, kmax = 5, 70, max(HUGE_LDA_K)
+    Ah, Bh = ints(rng, (m, kmax)), ints(rng, (kmax, n))
+    A_all = padded_device(Ah, 9_000_000)
+    B_all = torch.from_numpy(Bh).cuda()
+    for k in HUGE_LDA_K:
+        say("huge lda, stream-K, config", config, "k", k)
+        C = hta.sgemm_streamk(A_all[:, :k], B_all[:k], grid=3, config=config)
+        torch.cuda.synchronize()
+        assert_exact(C.cpu().numpy(), exact_product(Ah[:, :k], Bh[:k]),
+                     f"huge lda, stream-K, config {config}, k {k}")
+    del A_all, B_all
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("shape", [(1_000_000, 8, 16), (8, 1_000_000, 16), (3, 3, 1_000_003)],
                          ids=["tall", "wide", "long-k"])
 def test_extreme_aspect_ratios(shape):
