@@ -125,6 +125,25 @@ def test_streamk_long_k_without_direct_loads(config):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("config", [6, 9, 13])
+def test_splitk_long_k_without_direct_loads(config):
+    """The same operands through split-K partial slices (2 to 7 slices of
+    k = 1180): each slice's step count goes through the same tail dispatch."""
+    rng = np.random.default_rng(6)
+    m, n, k = 5, 70, 1180
+    Ah, Bh = ints(rng, (m, k)), ints(rng, (k, n))
+    A = padded_device(Ah, 9_000_000)[:, :k]
+    B = torch.from_numpy(Bh).cuda()
+    want = exact_product(Ah, Bh)
+    for splits in (2, 3, 5, 7):
+        say("huge lda, split-K, config", config, "splits", splits)
+        C = hta.sgemm_splitk(A, B, splits=splits, config=config)
+        torch.cuda.synchronize()
+        assert_exact(C.cpu().numpy(), want, f"huge lda, split-K, config {config}, {splits} slices")
+    del A, B
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("shape", [(1_000_000, 8, 16), (8, 1_000_000, 16), (3, 3, 1_000_003)],
                          ids=["tall", "wide", "long-k"])
 def test_extreme_aspect_ratios(shape):
