@@ -144,6 +144,23 @@ def test_splitk_long_k_without_direct_loads(config):
     torch.cuda.empty_cache()
 
 
+def test_valu_long_k_huge_lda():
+    """The register-tiled VALU kernel with lda = 9e6 floats (its offsets are
+    64-bit) over the same k values."""
+    rng = np.random.default_rng(7)
+    m, n, kmax = 5, 70, max(HUGE_LDA_K)
+    Ah, Bh = ints(rng, (m, kmax)), ints(rng, (kmax, n))
+    A_all = padded_device(Ah, 9_000_000)
+    B_all = torch.from_numpy(Bh).cuda()
+    for k in HUGE_LDA_K:
+        say("huge lda, VALU, k", k)
+        C = hta.sgemm_valu(A_all[:, :k], B_all[:k])
+        torch.cuda.synchronize()
+        assert_exact(C.cpu().numpy(), exact_product(Ah[:, :k], Bh[:k]), f"huge lda, VALU, k {k}")
+    del A_all, B_all
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("shape", [(1_000_000, 8, 16), (8, 1_000_000, 16), (3, 3, 1_000_003)],
                          ids=["tall", "wide", "long-k"])
 def test_extreme_aspect_ratios(shape):
