@@ -73,8 +73,9 @@ typedef enum mi_status {
  * mi_sgemm -- the matrix-core path.
  * Blocked through the memory hierarchy as described on page "GEMM优化原理",
  * sections "从 global memory 到 shared memory 再到 register" and
- * "prefetch 和双缓冲": workgroup tiles of A and B prefetched two k steps ahead
- * into a three-buffer LDS ring, per-wave tiles of C accumulated by FP32 MFMA
+ * "prefetch 和双缓冲": workgroup tiles of A and B prefetched one to three k
+ * steps ahead into an LDS ring of two to four buffers (three or four for the
+ * tiles the automatic choice uses), per-wave tiles of C accumulated by FP32 MFMA
  * instructions, and a grouped, XCD-aware workgroup order for L2 reuse (page
  * "gemm优化", section 杂项：预取缓存1， Swizzle 增强L2缓存命中).  The tile
  * configuration is chosen from the sizes of C (mi_sgemm_get_plan reports it).
