@@ -88,6 +88,11 @@ constexpr long long kSmallStepMinRounds = 8;
 // k = 900 on (3000 x 5000 x 1023: 123.5 -> 125.0, x 2047: 127.9 -> 130.5;
 // forced configurations, back to back on one MI355X).
 constexpr int kSmallStepDeepId = 13;
+// stream-K with one workgroup per CU (see plan_split)
+constexpr int kStreamKOnePerCuId = 6;
+constexpr int kStreamKOnePerCuMinK = 1024;
+constexpr int kStreamKOnePerCuMaxK = 2048;
+constexpr double kStreamKOnePerCuEfficiency = 0.95;  // one 4-wave workgroup per CU
 constexpr int kSmallStepDeepMinK = 848;
 
 int choose_mfma_config(int m, int n, int k) {
@@ -222,7 +227,8 @@ SplitPlan make_sk_plan(int m, int n, int k, int config, long long grid) {
 // workgroups share the matrix cores), one prologue / epilogue per tile or
 // segment, and the fixup reads the parts of at most grid - 1 shared tiles
 // (about ksteps / share + 1 parts each).
-double sk_cost_us(int m, int n, const SplitPlan &sp, double efficiency) {
+double sk_cost_us(int m, int n, const SplitPlan &sp, double efficiency,
+                  double seg_us = kWorkgroupOverheadUs) {
     (void)m;
     (void)n;
     const MfmaConfig &c = mfma_config(sp.config);
@@ -232,12 +238,12 @@ double sk_cost_us(int m, int n, const SplitPlan &sp, double efficiency) {
     const long long per_wg = rounds * sp.sk_ksteps + share;
     const long long per_cu = ceil_div(sp.sk_grid, kCUs);
     double t = (double)per_cu * per_wg * step_us;
-    if (share == 0) return t + (double)rounds * kWorkgroupOverheadUs;
+    if (share == 0) return t + (double)rounds * seg_us;
     const long long segments = rounds + ceil_div(share, sp.sk_ksteps) + 1;
     long long shared = sp.sk_grid - 1;
     if (shared > sp.sk_iters / sp.sk_ksteps) shared = sp.sk_iters / sp.sk_ksteps;
     const double parts = (double)sp.sk_ksteps / (double)share + 1.0;
-    return t + (double)segments * kWorkgroupOverheadUs + kCombineFixedUs +
+    return t + (double)segments * seg_us + kCombineFixedUs +
            4.0 * c.bm * c.bn * (double)shared * parts / kCombineBytesPerUs;
 }
 
@@ -281,6 +287,27 @@ SplitPlan plan_split(int m, int n, int k, int splits, int config, bool allow_sk 
             if (cost < best_cost * 0.97) {
                 best = sk;
                 best_cost = cost;
+            }
+        }
+        // The 64 x 64 x 32 tile on stream-K with one workgroup per CU
+        // instead of three: fewer, longer shares, and a segment's prologue
+        // and epilogue move a quarter of a 128 x 128 tile's data.  From
+        // k = 1024 on it beat the plans above on small grids (768^2 x 1024
+        // 47.2 -> 57.8, 1536^2 x 1536 107.1 -> 116.5 TFLOP/s, one MI355X);
+        // at k = 512 it lost.
+        if (allow_sk && id == kStreamKOnePerCuId && k >= kStreamKOnePerCuMinK &&
+            k <= kStreamKOnePerCuMaxK) {
+            const SplitPlan sk1 = make_sk_plan(m, n, k, id, kCUs);
+            if (sk1.sk_grid > 0 && 4 * (sk1.sk_iters / sk1.sk_grid) >= sk1.sk_ksteps &&
+                sk1.bytes <= kAutoWorkspaceCap) {
+                const MfmaConfig &c1 = mfma_config(id);
+                const double seg = kWorkgroupOverheadUs * (double)(c1.bm * c1.bn) / (128.0 * 128.0);
+                const double cost =
+                    sk_cost_us(m, n, sk1, config_efficiency(id) * kStreamKOnePerCuEfficiency, seg);
+                if (cost < best_cost * 0.97) {
+                    best = sk1;
+                    best_cost = cost;
+                }
             }
         }
     }

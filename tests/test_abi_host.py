@@ -277,6 +277,16 @@ def test_tile_choice_rules():
     assert config(3001, 4997, 1023) == 13                      # four buffers, long k
     assert config(2500, 6000, 847) == 12 and config(2500, 6000, 849) == 13
     assert config(2500, 6000, 777) == 12                       # three buffers, short k
+    # stream-K on the 64 x 64 x 32 tile with one workgroup per CU, for small
+    # grids with 1024 <= k <= 2048
+    def sk(m, n, k):
+        q = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, m, n, k, 0)
+        return q["config"], q["splits"], q["stream_k_grid"]
+    assert sk(768, 768, 1024) == (6, 1, 256)
+    assert sk(1536, 1536, 1024) == (6, 1, 256)
+    assert sk(1280, 1280, 1024) == (8, 1, 0)                   # the single pass stays
+    assert sk(1536, 1536, 4096) == (9, 1, 256)                 # k above the range
+    assert sk(768, 768, 512) == (6, 1, 0)                      # k below it: single pass
     # the split-K entry's single-slice plans use the same choice
     p = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, 8192, 8192, 8192, 0)
     assert p["splits"] == 1 and (p["tile_m"], p["tile_k"], p["threads"]) == (128, 16, 512)

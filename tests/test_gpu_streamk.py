@@ -163,3 +163,22 @@ def test_streamk_c_alignment(orc, off, ldc):
     ref = orc.sgemm(w.m, w.n, w.k, w.alpha, A, lda, B, ldb, w.beta, C, ldc)
     assert_exact(out[:, :w.n], ref["C"].reshape(w.m, ldc)[:, :w.n],
                  f"streamk C offset {off} ldc {ldc}")
+
+
+@pytest.mark.parametrize("shape", [(768, 768, 1024), (1536, 1536, 1024)],
+                         ids=["768x768x1024", "1536x1536x1024"])
+def test_streamk_auto_one_per_cu(orc, shape):
+    """Small grids with 1024 <= k <= 2048: the automatic split plan runs the
+    64 x 64 x 32 tile on stream-K with one workgroup per CU.  Integer operands
+    and beta != 0: bit-exact against the oracle on every element."""
+    m, n, k = shape
+    plan = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, m, n, k, 0)
+    assert (plan["config"], plan["stream_k_grid"]) == (6, 256)
+    w = synth.Workload(12, "skone", m, n, k, k, n, n, "uniform", "int3", 1.0, 0.5)
+    A, B, C = synth.operands(w, integer_twin=True)
+    say("streamk auto one per CU", m, n, k)
+    Ad, Bd, Cd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), torch.from_numpy(C).cuda()
+    hta.sgemm_splitk(Ad, Bd, Cd, alpha=1.0, beta=0.5, splits=0)
+    torch.cuda.synchronize()
+    ref = orc.sgemm(m, n, k, 1.0, A, k, B, n, 0.5, C, n)
+    assert_exact(Cd.cpu().numpy(), ref["C"].reshape(m, n), f"stream-K one per CU {m}x{n}x{k}")
