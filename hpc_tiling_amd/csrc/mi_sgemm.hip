@@ -92,7 +92,7 @@ constexpr int kSmallStepDeepId = 13;
 constexpr int kStreamKOnePerCuId = 6;
 constexpr int kStreamKOnePerCuMinK = 1024;
 constexpr int kStreamKOnePerCuMaxK = 2048;
-constexpr double kStreamKOnePerCuEfficiency = 0.95;  // one 4-wave workgroup per CU
+constexpr double kStreamKOnePerCuEfficiency = 0.97;  // one 4-wave workgroup per CU
 constexpr int kSmallStepDeepMinK = 848;
 
 int choose_mfma_config(int m, int n, int k) {
