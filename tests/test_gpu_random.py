@@ -22,7 +22,7 @@ else:
     hta = None
     N_CFG = 10
 
-CASES = 160
+CASES = 1000
 
 
 @pytest.fixture(scope="module", autouse=True)
