@@ -182,3 +182,10 @@ def test_streamk_auto_one_per_cu(orc, shape):
     torch.cuda.synchronize()
     ref = orc.sgemm(m, n, k, 1.0, A, k, B, n, 0.5, C, n)
     assert_exact(Cd.cpu().numpy(), ref["C"].reshape(m, n), f"stream-K one per CU {m}x{n}x{k}")
+    # float operands: the parts are added in a fixed order, so two runs agree bitwise
+    Af, Bf, _ = synth.operands(w)
+    Afd, Bfd = torch.from_numpy(Af).cuda(), torch.from_numpy(Bf).cuda()
+    C1 = hta.sgemm_splitk(Afd, Bfd, splits=0)
+    C2 = hta.sgemm_splitk(Afd, Bfd, splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
