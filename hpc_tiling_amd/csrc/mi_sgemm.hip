@@ -302,8 +302,12 @@ SplitPlan plan_split(int m, int n, int k, int splits, int config, bool allow_sk 
                 sk1.bytes <= kAutoWorkspaceCap) {
                 const MfmaConfig &c1 = mfma_config(id);
                 const double seg = kWorkgroupOverheadUs * (double)(c1.bm * c1.bn) / (128.0 * 128.0);
-                const double cost =
-                    sk_cost_us(m, n, sk1, config_efficiency(id) * kStreamKOnePerCuEfficiency, seg);
+                // (discounted only against a single pass or slices: where the
+                // plan so far is stream-K itself, the one-per-CU form won every
+                // measured case in this k range undiscounted)
+                const double eff = config_efficiency(id) *
+                                   (best.sk_grid > 0 ? 1.0 : kStreamKOnePerCuEfficiency);
+                const double cost = sk_cost_us(m, n, sk1, eff, seg);
                 if (cost < best_cost * 0.97) {
                     best = sk1;
                     best_cost = cost;

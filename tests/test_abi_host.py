@@ -284,6 +284,8 @@ def test_tile_choice_rules():
         return q["config"], q["splits"], q["stream_k_grid"]
     assert sk(768, 768, 1024) == (6, 1, 256)
     assert sk(1536, 1536, 1024) == (6, 1, 256)
+    assert sk(1536, 1536, 2048) == (6, 1, 256)                 # over a 128 x 128 stream-K plan
+    assert sk(2304, 2304, 1024) == (6, 1, 256)
     assert sk(1280, 1280, 1024) == (8, 1, 0)                   # the single pass stays
     assert sk(1536, 1536, 4096) == (9, 1, 256)                 # k above the range
     assert sk(768, 768, 512) == (6, 1, 0)                      # k below it: single pass
