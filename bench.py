@@ -337,7 +337,8 @@ def main(argv=None):
                  ("mfma_nt", "sgemm_2048x2048x2048"), ("mfma_tn", "sgemm_2048x2048x2048"),
                  ("mfma_tt", "sgemm_2048x2048x2048"), ("mfma_tt", "sgemm_8192x8192x8192_ab"),
                  ("splitk_tn", "sgemm_splitk_512x512x262144"),
-                 ("mfma", "sgemm_1536x1536x4096"), ("splitk", "sgemm_1536x1536x4096")]
+                 ("mfma", "sgemm_1536x1536x4096"), ("splitk", "sgemm_1536x1536x4096"),
+                 ("mfma", "sgemm_1536x1536x1024"), ("splitk", "sgemm_1536x1536x1024")]
         line["secondary"] = secondary(pairs)
         line["secondary"].append(reduce_secondary())
 

@@ -71,6 +71,10 @@ WORKLOADS = [
     # entry's plan runs it on the stream-K schedule
     Workload(5, "sgemm_1536x1536x4096", 1536, 1536, 4096, 4096, 1536, 1536,
              "uniform", None, 1.0, 0.0),
+    # a small grid with a short k: the split-K entry's plan runs the
+    # 64 x 64 x 32 tile on stream-K with one workgroup per CU
+    Workload(20, "sgemm_1536x1536x1024", 1536, 1536, 1024, 1024, 1536, 1536,
+             "uniform", None, 1.0, 0.0),
 ]
 
 
