@@ -22,8 +22,9 @@ __all__ = [
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
     "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex", "mi_sgemm_streamk",
-    "mi_sgemm_streamk_workspace_bytes",
-    "sgemm", "sgemm_streamk", "streamk_workspace", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace", "reduce_sum",
+    "mi_sgemm_streamk_workspace_bytes", "mi_sgemm_splitk_combine", "mi_clock_probe",
+    "mi_sgemm_with_order",
+    "sgemm", "sgemm_streamk", "streamk_workspace", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace", "splitk_combine", "reduce_sum", "ClockProbe",
     "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "KERNEL_SPLITK_ATOMIC", "EXPORTED_SYMBOLS",
     "OP_N", "OP_T",
 ]
@@ -52,7 +53,8 @@ EXPORTED_SYMBOLS = (
     "mi_sgemm_splitk_with_config", "mi_sgemm_splitk_with_config_workspace_bytes",
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
     "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex", "mi_sgemm_streamk",
-    "mi_sgemm_streamk_workspace_bytes",
+    "mi_sgemm_streamk_workspace_bytes", "mi_sgemm_splitk_combine", "mi_clock_probe",
+    "mi_sgemm_with_order",
 )
 
 if not LIB_PATH.exists():
@@ -101,6 +103,8 @@ lib.mi_sgemm_ex.argtypes = [_i, _i] + _GEMM_ARGS + [_vp]
 lib.mi_sgemm_ex.restype = _i
 lib.mi_sgemm_with_config.argtypes = [_i, _i, _i, _i] + _GEMM_ARGS + [_vp]
 lib.mi_sgemm_with_config.restype = _i
+lib.mi_sgemm_with_order.argtypes = [_i, _i, _i, _i, _i] + _GEMM_ARGS + [_vp]
+lib.mi_sgemm_with_order.restype = _i
 lib.mi_sgemm_splitk_workspace_bytes.argtypes = [_i, _i, _i, _i]
 lib.mi_sgemm_splitk_workspace_bytes.restype = _sz
 lib.mi_sgemm_splitk.argtypes = _GEMM_ARGS + [_i, _vp, _sz, _vp]
@@ -115,6 +119,10 @@ lib.mi_sgemm_streamk.argtypes = [_i, _i, _i] + _GEMM_ARGS + [_i, _vp, _sz, _vp]
 lib.mi_sgemm_streamk.restype = _i
 lib.mi_sgemm_streamk_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.mi_sgemm_streamk_workspace_bytes.restype = _sz
+lib.mi_sgemm_splitk_combine.argtypes = [_i, _i, _i, _vp, ctypes.c_longlong, _f, _f, _vp, _i, _vp]
+lib.mi_sgemm_splitk_combine.restype = _i
+lib.mi_clock_probe.argtypes = [_vp, _i, _i, ctypes.POINTER(_i), _vp]
+lib.mi_clock_probe.restype = _i
 lib.mi_sgemm_splitk_atomic.argtypes = _GEMM_ARGS + [_i, _vp]
 lib.mi_sgemm_splitk_atomic.restype = _i
 lib.mi_reduce_sum.argtypes = [ctypes.c_longlong, _vp, _vp, _vp, _sz, _vp]
@@ -160,6 +168,12 @@ def mi_sgemm_with_config(kernel, config, trans_a, trans_b, m, n, k, alpha, A, ld
                                     B, ldb, beta, C, ldc, stream)
 
 
+def mi_sgemm_with_order(config, xcd_remap, group_m, trans_a, trans_b, m, n, k, alpha, A, lda, B,
+                        ldb, beta, C, ldc, stream=None) -> int:
+    return lib.mi_sgemm_with_order(config, xcd_remap, group_m, trans_a, trans_b, m, n, k, alpha,
+                                   A, lda, B, ldb, beta, C, ldc, stream)
+
+
 def mi_sgemm_splitk_workspace_bytes(m, n, k, splits=0) -> int:
     return lib.mi_sgemm_splitk_workspace_bytes(m, n, k, splits)
 
@@ -200,6 +214,15 @@ def mi_sgemm_splitk_atomic(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits=
                            stream=None) -> int:
     return lib.mi_sgemm_splitk_atomic(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits,
                                       stream)
+
+
+def mi_sgemm_splitk_combine(m, n, splits, ws, slice, alpha, beta, C, ldc, stream=None) -> int:
+    return lib.mi_sgemm_splitk_combine(m, n, splits, ws, slice, alpha, beta, C, ldc, stream)
+
+
+def mi_clock_probe(ticks, workgroups, spin_us, ref_khz, stream=None) -> int:
+    """ref_khz: a ctypes.c_int (passed by reference)."""
+    return lib.mi_clock_probe(ticks, workgroups, spin_us, ctypes.byref(ref_khz), stream)
 
 
 def mi_reduce_sum(n, x, out, ws, ws_bytes, stream=None) -> int:
@@ -261,24 +284,6 @@ def _mat(t, name):
     raise ValueError(f"{name} must be row-major or column-major (one unit stride)")
 
 
-def _stream(stream, device):
-    """The HIP stream handle: `stream` (a torch stream or a raw handle), else
-    the current stream of device index `device`."""
-    import torch
-    if stream is None:
-        return torch._C._cuda_getCurrentRawStream(device)
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-
-
-def _device_of(*tensors):
-    """The one device all given tensors (None skipped) live on; tensors on
-    different devices are refused."""
-    devs = {t.device for t in tensors if t is not None}
-    if len(devs) != 1:
-        raise ValueError(f"tensors are on different devices: {sorted(str(d) for d in devs)}")
-    return devs.pop()
-
-
 class _Unchanged:
     def __enter__(self):
         return self
@@ -288,6 +293,54 @@ class _Unchanged:
 
 
 _UNCHANGED = _Unchanged()
+
+
+def _stream(stream, device):
+    """The HIP stream handle: `stream` (a torch stream or a raw handle), else
+    the current stream of device index `device`."""
+    import torch
+    if stream is None:
+        return torch._C._cuda_getCurrentRawStream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _tensor_device(t, name):
+    """Device index of tensor `t` (checked again, with the other properties,
+    when its layout is read)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    dev = t.get_device()
+    if dev < 0:
+        raise ValueError(f"{name} must be a device tensor")
+    return dev
+
+
+def _on_stream(stream, device):
+    """A context in which `stream` (None: the current stream, nothing
+    changes) is torch's current stream on device index `device`.  The helpers
+    allocate C and workspaces inside it, so the caching allocator ties those
+    blocks to the stream the kernels run on: a block freed on return is
+    handed out again only to work ordered after those kernels on that
+    stream."""
+    import torch
+    if stream is None:
+        return _UNCHANGED
+    if not isinstance(stream, torch.cuda.Stream):
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        if handle == torch._C._cuda_getCurrentRawStream(device):
+            return _UNCHANGED
+        stream = torch.cuda.ExternalStream(handle, device=device)
+    return torch.cuda.stream(stream)
+
+
+def _device_of(*tensors):
+    """The one device all given tensors (None skipped) live on; tensors on
+    different devices are refused."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"tensors are on different devices: {sorted(str(d) for d in devs)}")
+    return devs.pop()
 
 
 def _current(dev):
@@ -345,15 +398,21 @@ def _prepare_ex(A, B, C, beta):
     return (1 - tb, 1 - ta, n, m, k, pb, ldb, pa, lda), C, pc, ldc, dev
 
 
-def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
+def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None, order=None):
     """C <- alpha * A @ B + beta * C on the matrix cores; returns C.
     A (m x k), B (k x n), C (m x n): float32 device tensors, each row-major
     or column-major (a transposed view such as ``X.t()`` is passed as the
-    transposed operand, without a copy)."""
-    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev = _prepare_ex(A, B, C, beta)
-    with _current(dev):
-        s = _stream(stream, dev)
-        if config is None:
+    transposed operand, without a copy).  `order` = (xcd_remap, group_m)
+    forces the workgroup order (mi_sgemm_with_order)."""
+    dev = _tensor_device(A, "A")
+    with _current(dev), _on_stream(stream, dev):
+        (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev = _prepare_ex(A, B, C, beta)
+        s = _stream(None, dev)
+        if order is not None:
+            st = lib.mi_sgemm_with_order(-1 if config is None else config, order[0], order[1],
+                                         ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc,
+                                         ldc, s)
+        elif config is None:
             st = lib.mi_sgemm_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, s)
         else:
             st = lib.mi_sgemm_with_config(KERNEL_MFMA, config, ta, tb, m, n, k, alpha, pa, lda,
@@ -366,10 +425,11 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
 def sgemm_valu(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
     """Same as sgemm (row-major operands only), on the register-tiled VALU
     kernel."""
-    m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _prepare(A, B, C, beta)
-    with _current(dev):
+    dev = _tensor_device(A, "A")
+    with _current(dev), _on_stream(stream, dev):
+        m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _prepare(A, B, C, beta)
         st = lib.mi_sgemm_valu(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
-                               _stream(stream, dev))
+                               _stream(None, dev))
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_valu")
     return C
@@ -391,13 +451,14 @@ def sgemm_splitk(A, B, C=None, alpha=1.0, beta=0.0, splits=0, workspace=None, st
     """Same as sgemm with the k range split into slices; `workspace` is a
     device tensor of at least mi_sgemm_splitk_workspace_bytes bytes (allocated
     here when None).  `config` forces the partial kernel's tile configuration."""
-    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev = _prepare_ex(A, B, C, beta)
-    if workspace is None:
-        workspace = splitk_workspace(m, n, k, splits, device=A.device, config=config)
-    _same_device(dev, workspace)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    with _current(dev):
-        s = _stream(stream, dev)
+    dev = _tensor_device(A, "A")
+    with _current(dev), _on_stream(stream, dev):
+        (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev = _prepare_ex(A, B, C, beta)
+        if workspace is None:
+            workspace = splitk_workspace(m, n, k, splits, device=A.device, config=config)
+        _same_device(dev, workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        s = _stream(None, dev)
         if config is None:
             st = lib.mi_sgemm_splitk_ex(ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
                                         splits, workspace.data_ptr(), ws_bytes, s)
@@ -421,14 +482,15 @@ def sgemm_streamk(A, B, C=None, alpha=1.0, beta=0.0, grid=0, workspace=None, str
                   config=-1):
     """Same as sgemm on a forced stream-K schedule (`grid` workgroups, 0 for
     one per resident slot of every CU); `workspace` as streamk_workspace."""
-    (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev = _prepare_ex(A, B, C, beta)
-    if workspace is None:
-        workspace = streamk_workspace(m, n, k, grid, device=A.device, config=config)
-    _same_device(dev, workspace)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    with _current(dev):
+    dev = _tensor_device(A, "A")
+    with _current(dev), _on_stream(stream, dev):
+        (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, dev = _prepare_ex(A, B, C, beta)
+        if workspace is None:
+            workspace = streamk_workspace(m, n, k, grid, device=A.device, config=config)
+        _same_device(dev, workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
         st = lib.mi_sgemm_streamk(config, ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc,
-                                  ldc, grid, workspace.data_ptr(), ws_bytes, _stream(stream, dev))
+                                  ldc, grid, workspace.data_ptr(), ws_bytes, _stream(None, dev))
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_streamk")
     return C
@@ -437,13 +499,65 @@ def sgemm_streamk(A, B, C=None, alpha=1.0, beta=0.0, grid=0, workspace=None, str
 def sgemm_splitk_atomic(A, B, C=None, alpha=1.0, beta=0.0, splits=0, stream=None):
     """Split-K with atomic accumulation into C (row-major operands; no
     workspace; not bitwise reproducible run to run)."""
-    m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _prepare(A, B, C, beta)
-    with _current(dev):
+    dev = _tensor_device(A, "A")
+    with _current(dev), _on_stream(stream, dev):
+        m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _prepare(A, B, C, beta)
         st = lib.mi_sgemm_splitk_atomic(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, splits,
-                                        _stream(stream, dev))
+                                        _stream(None, dev))
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_splitk_atomic")
     return C
+
+
+def splitk_combine(parts, C, alpha=1.0, beta=0.0, stream=None):
+    """C <- alpha * parts.sum(0) + beta * C through mi_sgemm_splitk_combine.
+    parts: float32 device tensor (S, m, n) or (S, slice) with contiguous
+    slices (16-byte aligned, slice a multiple of 4 and >= m*n rounded up to
+    4); C: m x n row-major float32 device tensor (row stride = ldc)."""
+    import torch
+    if not isinstance(parts, torch.Tensor) or parts.dtype != torch.float32 or not parts.is_cuda:
+        raise TypeError("parts must be a float32 device tensor")
+    S = parts.shape[0]
+    slice_ = parts.stride(0) if S > 1 else max(parts[0].numel(), 4)
+    dev = parts.get_device()
+    pc, ldc, tc, m, n, dc = _mat(C, "C")
+    if tc != OP_N:
+        raise ValueError("C must be row-major (unit column stride)")
+    _same_device(dev, C)
+    with _current(dev):
+        st = lib.mi_sgemm_splitk_combine(m, n, S, parts.data_ptr(), slice_, alpha, beta, pc,
+                                         ldc, _stream(stream, dev))
+    if st != SUCCESS:
+        raise MiSgemmError(st, "mi_sgemm_splitk_combine")
+    return C
+
+
+class ClockProbe:
+    """Core clock measured on the GPU in stream order (mi_clock_probe): call
+    launch() where the clock is wanted, and mhz() after synchronising."""
+
+    def __init__(self, workgroups=8, spin_us=20, device=None):
+        import torch
+        self.workgroups, self.spin_us = workgroups, spin_us
+        self.ticks = torch.zeros(4 * workgroups, dtype=torch.int64, device=device or "cuda")
+        self.ref_khz = ctypes.c_int(0)
+
+    def launch(self, stream=None):
+        dev = self.ticks.get_device()
+        with _current(dev):
+            st = lib.mi_clock_probe(self.ticks.data_ptr(), self.workgroups, self.spin_us,
+                                    ctypes.byref(self.ref_khz), _stream(stream, dev))
+        if st != SUCCESS:
+            raise MiSgemmError(st, "mi_clock_probe")
+
+    def mhz(self):
+        """Per-workgroup clocks in MHz of the last launch (host list)."""
+        t = self.ticks.cpu().tolist()
+        out = []
+        for w in range(self.workgroups):
+            c0, r0, c1, r1 = t[4 * w:4 * w + 4]
+            out.append((c1 - c0) / max(r1 - r0, 1) * self.ref_khz.value / 1e3)
+        return out
 
 
 def reduce_sum(x, out=None, workspace=None, stream=None):
@@ -455,17 +569,17 @@ def reduce_sum(x, out=None, workspace=None, stream=None):
     if x.dim() != 1 or (x.numel() > 1 and x.stride(0) != 1):
         raise ValueError("x must be 1-D and contiguous")
     n = x.numel()
-    if out is None:
-        out = torch.empty(1, dtype=torch.float32, device=x.device)
-    if workspace is None:
-        workspace = torch.empty(max(mi_reduce_sum_workspace_bytes(n), 4), dtype=torch.uint8,
-                                device=x.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
     dev = x.get_device()
-    _same_device(dev, out, workspace)
-    with _current(dev):
+    with _current(dev), _on_stream(stream, dev):
+        if out is None:
+            out = torch.empty(1, dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(max(mi_reduce_sum_workspace_bytes(n), 4), dtype=torch.uint8,
+                                    device=x.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        _same_device(dev, out, workspace)
         st = lib.mi_reduce_sum(n, x.data_ptr() if n else None, out.data_ptr(),
-                               workspace.data_ptr(), ws_bytes, _stream(stream, dev))
+                               workspace.data_ptr(), ws_bytes, _stream(None, dev))
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_reduce_sum")
     return out

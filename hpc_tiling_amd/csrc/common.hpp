@@ -38,6 +38,8 @@ struct GemmArgs {
     long long sk_iters;    // stream-K: (shared tiles) * k steps per tile
     int sk_ksteps;         // stream-K: k steps per tile
     int sk_dp_tiles;       // stream-K: leading tiles computed whole, one per workgroup
+    int xcd_remap;         // 1: logical ids contiguous per XCD (xcd_contiguous); 0: the
+                           // hardware order (measured comparisons only)
 };
 
 // Stream-K partition of `iters` (tile, k step) iterations over `grid`

@@ -14,6 +14,7 @@
 #include "sgemm_valu.hpp"
 #include "reduce.hpp"
 #include "splitk.hpp"
+#include "clock.hpp"
 
 namespace mi {
 namespace {
@@ -394,6 +395,17 @@ int launch_scale(int m, int n, float beta, float *C, int ldc, hipStream_t stream
     return launch_raw(reinterpret_cast<const void *>(&scale_c_kernel), blocks, 256, args, stream);
 }
 
+// The combine of `splits` partial slices (arguments checked).  It walks its
+// chunks grid-stride, so the block count is capped.
+int launch_combine(int m, int n, int splits, const float *ws, long long slice, float alpha,
+                   float beta, float *C, int ldc, hipStream_t s) {
+    const long long blocks =
+        std::min(ceil_div(ceil_div((long long)m * n, 64), 4), kCombineMaxBlocks);
+    long long ldc64 = ldc;
+    void *args[] = {&ws, &slice, &splits, &m, &n, &alpha, &beta, &C, &ldc64};
+    return launch_raw(reinterpret_cast<const void *>(&splitk_combine_kernel), blocks, 256, args, s);
+}
+
 GemmArgs base_args(int m, int n, int k, float alpha, const float *A, int lda, const float *B,
                    int ldb, float beta, float *C, int ldc) {
     GemmArgs a;
@@ -402,6 +414,7 @@ GemmArgs base_args(int m, int n, int k, float alpha, const float *A, int lda, co
     a.alpha = alpha; a.beta = beta;
     a.A = A; a.lda = lda; a.B = B; a.ldb = ldb; a.C = C; a.ldc = ldc;
     a.group_m = kGroupM;
+    a.xcd_remap = 1;
     a.c_vec = aligned16(C) && ldc % 4 == 0;
     return a;
 }
@@ -424,11 +437,21 @@ int prologue(int m, int n, int k, float alpha, const float *A, int lda, const fl
     return MI_SGEMM_SUCCESS;
 }
 
-// The full-k matrix-core kernel of configuration `id` (arguments checked).
+// The full-k matrix-core kernel of configuration `id` (arguments checked),
+// in the grouped, XCD-aware workgroup order unless `order` overrides it
+// ({xcd_remap, group_m}, measured comparisons only).
+struct TileOrder {
+    int xcd_remap, group_m;
+};
+constexpr TileOrder kDefaultOrder{1, kGroupM};
+
 int launch_full(int id, int ta, int tb, int m, int n, int k, float alpha, const float *A, int lda,
-                const float *B, int ldb, float beta, float *C, int ldc, hipStream_t s) {
+                const float *B, int ldb, float beta, float *C, int ldc, hipStream_t s,
+                TileOrder order = kDefaultOrder) {
     const MfmaConfig &c = mfma_config(id);
     GemmArgs a = base_args(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
+    a.xcd_remap = order.xcd_remap;
+    a.group_m = order.group_m;
     a.tiles_m = (int)ceil_div(m, c.bm);
     a.tiles_n = (int)ceil_div(n, c.bn);
     const long long grid = (long long)a.tiles_m * a.tiles_n;
@@ -436,14 +459,15 @@ int launch_full(int id, int ta, int tb, int m, int n, int k, float alpha, const 
 }
 
 int run_mfma(int config, int ta, int tb, int m, int n, int k, float alpha, const float *A,
-             int lda, const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+             int lda, const float *B, int ldb, float beta, float *C, int ldc, void *stream,
+             TileOrder order = kDefaultOrder) {
     if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     bool done;
     int st = prologue(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, &done, ta, tb);
     if (st || done) return st;
     const int id = config < 0 ? choose_mfma_config(m, n, k) : config;
-    return launch_full(id, ta, tb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    return launch_full(id, ta, tb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, order);
 }
 
 int run_valu(int config, int m, int n, int k, float alpha, const float *A, int lda,
@@ -524,14 +548,7 @@ int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, con
     st = launch(c.split[ta][tb][vector_ok(A, lda, B, ldb)], grid, 64 * c.wgm * c.wgn, s, a);
     if (st) return st;
 
-    // (the combine walks its chunks grid-stride, so the block count is capped)
-    const long long blocks =
-        std::min(ceil_div(ceil_div((long long)m * n, 64), 4), kCombineMaxBlocks);
-    const float *wsc = wsa;
-    long long slice = sp.slice, ldc64 = ldc;
-    int nsplit = sp.splits;
-    void *args[] = {&wsc, &slice, &nsplit, &m, &n, &alpha, &beta, &C, &ldc64};
-    return launch_raw(reinterpret_cast<const void *>(&splitk_combine_kernel), blocks, 256, args, s);
+    return launch_combine(m, n, sp.splits, wsa, sp.slice, alpha, beta, C, ldc, s);
 }
 
 // Split-K without a workspace: C <- beta*C, then every (tile, slice)
@@ -655,6 +672,14 @@ int mi_sgemm_with_config(int kernel, int config, int trans_a, int trans_b, int m
     return MI_SGEMM_ERROR_INVALID_VALUE;
 }
 
+int mi_sgemm_with_order(int config, int xcd_remap, int group_m, int trans_a, int trans_b, int m,
+                        int n, int k, float alpha, const float *A, int lda, const float *B,
+                        int ldb, float beta, float *C, int ldc, void *stream) {
+    if ((xcd_remap != 0 && xcd_remap != 1) || group_m < 1) return MI_SGEMM_ERROR_INVALID_VALUE;
+    return run_mfma(config, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                    stream, TileOrder{xcd_remap, group_m});
+}
+
 size_t mi_sgemm_splitk_workspace_bytes(int m, int n, int k, int splits) {
     return mi_sgemm_splitk_with_config_workspace_bytes(-1, m, n, k, splits);
 }
@@ -705,6 +730,25 @@ size_t mi_sgemm_splitk_with_config_workspace_bytes(int config, int m, int n, int
     return plan_split(m, n, k, splits, config).bytes;
 }
 
+int mi_sgemm_splitk_combine(int m, int n, int splits, const float *ws, long long slice,
+                            float alpha, float beta, float *C, int ldc, void *stream) {
+    if (m < 0 || n < 0 || splits < 0) return MI_SGEMM_ERROR_INVALID_VALUE;
+    if (ldc < (n > 1 ? n : 1)) return MI_SGEMM_ERROR_INVALID_LD;
+    if (m == 0 || n == 0) return MI_SGEMM_SUCCESS;
+    if (!C || (splits > 0 && alpha != 0.f && !ws)) return MI_SGEMM_ERROR_NULL_POINTER;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (splits == 0 || alpha == 0.f) {
+        const int st = check_device();
+        return st ? st : launch_scale(m, n, beta, C, ldc, s);
+    }
+    // every float4 a lane reads lies inside its slice
+    const long long mn = (long long)m * n;
+    if (slice % 4 != 0 || slice < ceil_div(mn, 4) * 4 || !aligned16(ws))
+        return MI_SGEMM_ERROR_INVALID_VALUE;
+    const int st = check_device();
+    return st ? st : launch_combine(m, n, splits, ws, slice, alpha, beta, C, ldc, s);
+}
+
 size_t mi_reduce_sum_workspace_bytes(long long n) {
     if (n <= 0) return 0;
     return (size_t)reduce_grid(n) * sizeof(float);
@@ -745,6 +789,27 @@ int mi_reduce_sum(long long n, const float *x, float *out, void *ws, size_t ws_b
     void *args[] = {&pc, &count, &out};
     return launch_raw(reinterpret_cast<const void *>(&reduce_final_kernel), 1, kFinalThreads,
                       args, s);
+}
+
+int mi_clock_probe(unsigned long long *ticks, int workgroups, int spin_us, int *ref_khz,
+                   void *stream) {
+    if (workgroups < 1 || workgroups > kClockProbeMaxWorkgroups || spin_us < 1 ||
+        spin_us > 100000)
+        return MI_SGEMM_ERROR_INVALID_VALUE;
+    if (!ticks || !ref_khz) return MI_SGEMM_ERROR_NULL_POINTER;
+    int st = check_device();
+    if (st) return st;
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz <= 0)
+        return MI_SGEMM_ERROR_DEVICE;
+    *ref_khz = khz;
+    long long spin = (long long)spin_us * khz / 1000;
+    if (spin < 1) spin = 1;
+    void *args[] = {&ticks, &spin};
+    return launch_raw(reinterpret_cast<const void *>(&clock_probe_kernel), workgroups, 64, args,
+                      static_cast<hipStream_t>(stream));
 }
 
 const char *mi_status_string(int status) {

@@ -52,6 +52,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "kloop.hpp"
 
 namespace mi {
 
@@ -226,9 +227,6 @@ __device__ __forceinline__ void barrier_keep_newest() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
-
-// What a step loads for the step DIST ahead (see one_step in the kernel).
-constexpr int kLoadNone = 0, kLoadDirect = 1, kLoadRegs = 2, kLoadAuto = 3;
 
 // Epilogue modes.  kFull: the whole k range, C = alpha*acc + beta*C.
 // kPartial: workgroup (tile, slice) sums k in [slice*k_per_split, ...) into
@@ -462,7 +460,7 @@ void sgemm_mfma_kernel(GemmArgs p) {
         Frag f[2];
         // load the tile of one of the first D steps
         auto fill = [&](int step, auto buf) {
-            if (step < ndirect) {
+            if (load_of(step, nsteps, ndirect) == kLoadDirect) {
                 load_direct(step, buf);
             } else {
                 Stage st;
@@ -507,8 +505,9 @@ void sgemm_mfma_kernel(GemmArgs p) {
             constexpr int CUR = decltype(cur)::value;
             using NXT = std::integral_constant<int, (CUR + 1) % NS>;  // (step + 1) % NS
             using WRT = std::integral_constant<int, (CUR + D) % NS>;  // (step + D) % NS
-            const bool ahead = LOAD == kLoadAuto ? step + D < nsteps : LOAD != kLoadNone;
-            const bool direct = LOAD == kLoadAuto ? step + D < ndirect : LOAD == kLoadDirect;
+            const int load = LOAD == kLoadAuto ? load_of(step + D, nsteps, ndirect) : LOAD;
+            const bool ahead = load != kLoadNone;
+            const bool direct = load == kLoadDirect;
             Stage st;
             if (!direct && ahead) load_regs(st, step + D);
             if (LOAD_GROUP == 0 && direct) load_direct(step + D, WRT{});
@@ -547,11 +546,13 @@ void sgemm_mfma_kernel(GemmArgs p) {
         using S3 = std::integral_constant<int, 3>;
         using LD = std::integral_constant<int, kLoadDirect>;
         using LA = std::integral_constant<int, kLoadAuto>;
+        // The phases of the run and its tail sequence (kloop.hpp).
+        const KLoop kl = kloop_schedule(nsteps, ndirect, NS);
         int step = 0;
         // Steady state: NS steps per iteration, so each ring position is a
         // compile-time constant and the accumulators keep their registers
         // (a runtime switch per step makes the compiler copy them around).
-        for (; step + NS - 1 + D < ndirect; step += NS) {
+        for (; step < kl.steady_end; step += NS) {
             one_step(step, LD{}, S0{});
             one_step(step + 1, LD{}, S1{});
             if constexpr (NS > 2) one_step(step + 2, LD{}, S2{});
@@ -559,24 +560,24 @@ void sgemm_mfma_kernel(GemmArgs p) {
         }
         // Without direct loads (huge leading dimensions) whole rounds of the
         // ring go through the deciding step too, so step % NS stays 0.
-        for (; nsteps - step > 5; step += NS) {
+        for (; step < kl.auto_end; step += NS) {
             one_step(step, LA{}, S0{});
             one_step(step + 1, LA{}, S1{});
             if constexpr (NS > 2) one_step(step + 2, LA{}, S2{});
             if constexpr (NS > 3) one_step(step + 3, LA{}, S3{});
         }
-        // The last R <= 5 steps (step % NS == 0 here), ND of them whole k
+        // The last R <= kTailMax steps (step % NS == 0 here), ND of them whole k
         // steps, as one of a few sequences fixed at compile time: step i
         // loads step i + D directly, through VGPRs (the partial step) or not
         // at all.  Decided in each step at run time, they ran about a
         // quarter of a step slower each.
-        auto tail = [&](auto r_tag, auto nd_tag) {
-            constexpr int R = decltype(r_tag)::value, ND = decltype(nd_tag)::value;
+        auto tail = [&](auto seq_tag) {
+            constexpr TailSeq SEQ = kTailSequences[decltype(seq_tag)::value];
             auto at = [&](auto i_tag) {
                 constexpr int I = decltype(i_tag)::value;
-                if constexpr (I < R) {
-                    constexpr int L = I + D >= R ? kLoadNone : (I + D < ND ? kLoadDirect : kLoadRegs);
-                    one_step(step + I, std::integral_constant<int, L>{},
+                if constexpr (I < SEQ.r) {
+                    one_step(step + I,
+                             std::integral_constant<int, load_of(I + D, SEQ.r, SEQ.nd)>{},
                              std::integral_constant<int, I % NS>{});
                 }
             };
@@ -586,6 +587,7 @@ void sgemm_mfma_kernel(GemmArgs p) {
             at(std::integral_constant<int, 3>{});
             at(std::integral_constant<int, 4>{});
         };
+        static_assert(kTailMax == 5, "the tail steps cover five steps");
         auto tail_auto = [&]() {
             using Q2 = std::integral_constant<int, 2 % NS>;
             using Q3 = std::integral_constant<int, 3 % NS>;
@@ -596,34 +598,25 @@ void sgemm_mfma_kernel(GemmArgs p) {
             if (step + 3 < nsteps) one_step(step + 3, LA{}, Q3{});
             if (step + 4 < nsteps) one_step(step + 4, LA{}, Q4{});
         };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        using I3 = std::integral_constant<int, 3>;
-        using I4 = std::integral_constant<int, 4>;
-        using I5 = std::integral_constant<int, 5>;
-        const int rem = nsteps - step, nd = ndirect - step;
-        // (rem, nd): nd is rem or rem - 1 when direct loads are used.  Without
-        // them (ndirect == 0: offsets beyond the buffer range) nd is -step,
-        // which must not reach the switch: its key would alias another
-        // (steps, whole steps) pair, running too few steps and issuing
-        // direct loads.  Two-buffer rings (long k steps per tile, registers
-        // to the limit) keep the run-time tail.
+        // The sequence kl.tail, each one compiled in its own branch.
+        auto dispatch = [&](auto self, auto idx_tag) {
+            constexpr int IDX = decltype(idx_tag)::value;
+            if constexpr (IDX < kNumTailSequences) {
+                if (kl.tail == IDX)
+                    tail(idx_tag);
+                else
+                    self(self, std::integral_constant<int, IDX + 1>{});
+            } else {
+                tail_auto();
+            }
+        };
+        // Two-buffer rings (long k steps per tile, registers to the limit)
+        // keep the run-time tail (kloop_schedule never picks a sequence
+        // for them).
         if constexpr (NS == 2) {
             tail_auto();
-        } else if (nd != rem && nd != rem - 1) {
-            tail_auto();
-        } else switch (rem * 8 + nd) {
-            case 1 * 8 + 0: tail(I1{}, I0{}); break;
-            case 1 * 8 + 1: tail(I1{}, I1{}); break;
-            case 2 * 8 + 1: tail(I2{}, I1{}); break;
-            case 2 * 8 + 2: tail(I2{}, I2{}); break;
-            case 3 * 8 + 2: tail(I3{}, I2{}); break;
-            case 3 * 8 + 3: tail(I3{}, I3{}); break;
-            case 4 * 8 + 3: tail(I4{}, I3{}); break;
-            case 4 * 8 + 4: tail(I4{}, I4{}); break;
-            case 5 * 8 + 4: tail(I5{}, I4{}); break;
-            default: tail_auto(); break;
+        } else {
+            dispatch(dispatch, std::integral_constant<int, 0>{});
         }
     }
     };
@@ -701,7 +694,7 @@ void sgemm_mfma_kernel(GemmArgs p) {
             it += ke - ks;
         }
     } else {
-        int id = xcd_contiguous(blockIdx.x, gridDim.x);
+        int id = p.xcd_remap ? xcd_contiguous(blockIdx.x, gridDim.x) : (int)blockIdx.x;
         int slice = 0;
         if (SPLIT) {
             const int tiles = p.tiles_m * p.tiles_n;

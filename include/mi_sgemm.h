@@ -123,9 +123,16 @@ int mi_sgemm_valu(int m, int n, int k, float alpha,
 /*
  * mi_sgemm_splitk_workspace_bytes -- bytes of device workspace that
  * mi_sgemm_splitk needs for these sizes and this split request (splits = 0
- * asks the library to choose).  Returns 0 when no workspace is needed
- * (m == 0, n == 0 or k == 0, or a plan of one slice) and also for invalid
- * arguments (m, n, k < 0, splits < 0 or splits > k).
+ * asks the library to choose).  The workspace holds the raw partial sums of
+ * the S slices of the big iteration over K (page "GEMM优化原理", section
+ * 基于 shared memory 计算): S slices of m * n floats, each slice rounded up
+ * to a multiple of 64 floats, plus 256 bytes so that the slices can start on
+ * a 256-byte boundary inside any buffer -- S * ceil(m*n / 64) * 64 * 4 + 256
+ * bytes.  When the plan is the stream-K schedule instead (plan field
+ * stream_k_grid > 0) it is two tiles of floats per stream-K workgroup, plus
+ * the same 256 bytes.  Returns 0 when no workspace is needed (m == 0,
+ * n == 0 or k == 0, or a plan of one slice) and also for invalid arguments
+ * (m, n, k < 0, splits < 0 or splits > k).
  */
 size_t mi_sgemm_splitk_workspace_bytes(int m, int n, int k, int splits);
 
@@ -164,6 +171,25 @@ int mi_sgemm_splitk_ex(int trans_a, int trans_b, int m, int n, int k, float alph
                        const float *A, int lda, const float *B, int ldb,
                        float beta, float *C, int ldc,
                        int splits, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * mi_sgemm_splitk_combine -- the second pass of mi_sgemm_splitk on its own:
+ *     C_ij <- alpha * sum_{s < splits} ws[s * slice + i * n + j] + beta * C_ij
+ * over the logical m x n extent of C (partial sums stored densely, row-major
+ * with row length n, slice after slice).  The slices are added in two levels:
+ * each lane sums a strided subset of them, then cross-lane exchanges of the
+ * wavefront add the lanes' sums (page aerisun.top, sections
+ * "先在线程内累加，再交换部分和" and "Warp shuffle 的数据交换"); the order is
+ * fixed, so the result is the same bits on every run.  ws: device memory,
+ * 16-byte aligned, read-only; slice: floats between the starts of two slices,
+ * a multiple of 4 and at least m * n rounded up to a multiple of 4 (the
+ * entries past m * n are read but not used).  beta == 0 writes C without
+ * reading it; splits == 0 or alpha == 0 gives C <- beta * C without reading
+ * ws.  Errors: INVALID_VALUE (m, n or splits < 0, or ws / slice outside the
+ * rules above), INVALID_LD (ldc < max(1, n)), NULL_POINTER, LAUNCH, DEVICE.
+ */
+int mi_sgemm_splitk_combine(int m, int n, int splits, const float *ws, long long slice,
+                            float alpha, float beta, float *C, int ldc, void *stream);
 
 /*
  * mi_sgemm_splitk_atomic -- split-K without a workspace, kept as a measured
@@ -208,7 +234,38 @@ size_t mi_reduce_sum_workspace_bytes(long long n);
  */
 long long mi_reduce_sum_max_additions(long long n);
 
-/* Text for a mi_status value (a static string; never NULL). */
+/* ------------------------------------------------------------------------
+ * Clock measurement.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * mi_clock_probe -- measures the core clock on the GPU, in stream order (so
+ * it reports the clock right before or after the kernels around it).  Page
+ * "gemm优化" (blog.lightlisten.com), section 关于GPU频率影响, shows timings
+ * changing with the core clock; this gives each timing its clock.  Each of
+ * `workgroups` workgroups (placed on the XCDs round-robin: 8 cover each XCD
+ * once) reads the shader-cycle counter and the constant-rate reference
+ * counter, waits about spin_us microseconds, and reads both again:
+ *     ticks[4w + 0] shader cycles at the start,  ticks[4w + 1] reference ticks,
+ *     ticks[4w + 2] shader cycles at the end,    ticks[4w + 3] reference ticks;
+ * the clock of workgroup w in MHz is
+ *     (ticks[4w+2] - ticks[4w]) / (ticks[4w+3] - ticks[4w+1]) * ref_khz / 1000.
+ * ticks: device memory for 4 * workgroups unsigned 64-bit values (written);
+ * ref_khz: host int, receives the reference counter's rate in kHz.
+ * Errors: INVALID_VALUE (workgroups outside 1..1024, spin_us outside
+ * 1..100000), NULL_POINTER, DEVICE, LAUNCH.
+ */
+int mi_clock_probe(unsigned long long *ticks, int workgroups, int spin_us, int *ref_khz,
+                   void *stream);
+
+/*
+ * Text for a mi_status value (a static string; never NULL).  The statuses
+ * report the preconditions that page "GPU 访存与计算优化" (aerisun.top),
+ * section "float4 向量化的条件", states for a vectorised kernel -- sizes that
+ * are not negative, indices that do not overflow, arrays that hold the
+ * elements addressed -- checked here before any launch instead of assumed;
+ * alignment is not a precondition (unaligned operands take 4-byte loads).
+ */
 const char *mi_status_string(int status);
 
 /* ------------------------------------------------------------------------
@@ -281,6 +338,25 @@ int mi_sgemm_with_config(int kernel, int config, int trans_a, int trans_b,
                          int m, int n, int k, float alpha,
                          const float *A, int lda, const float *B, int ldb,
                          float beta, float *C, int ldc, void *stream);
+
+/*
+ * mi_sgemm_with_order -- mi_sgemm_with_config (matrix-core kernel) with the
+ * workgroup order forced, for measured comparisons of the order against L2
+ * reuse (page "gemm优化", section 杂项：预取缓存1， Swizzle 增强L2缓存命中).
+ * The default order is xcd_remap = 1, group_m = 8: the workgroup ids the
+ * hardware deals out to the 8 XCDs round-robin are renumbered so that each
+ * XCD owns one contiguous range of tiles, and consecutive tiles walk down
+ * groups of group_m tile rows before moving to the next tile column.
+ * xcd_remap = 0 keeps the hardware numbering; group_m = 1 walks the tiles in
+ * plain row-major order.  The order decides only which workgroup computes
+ * which tile: the result is bitwise that of every other order.  config: as
+ * mi_sgemm_with_config (< 0: automatic).  Errors as mi_sgemm_ex, plus
+ * INVALID_VALUE for xcd_remap other than 0 or 1 or group_m < 1.
+ */
+int mi_sgemm_with_order(int config, int xcd_remap, int group_m, int trans_a, int trans_b,
+                        int m, int n, int k, float alpha,
+                        const float *A, int lda, const float *B, int ldb,
+                        float beta, float *C, int ldc, void *stream);
 
 /*
  * mi_sgemm_splitk_with_config -- mi_sgemm_splitk with a forced tile

@@ -76,26 +76,16 @@ class Oracle:
             build(out=path)
         self.path = path
         lib = ctypes.CDLL(str(path))
-        lib.oracle_sgemm_rows.restype = ctypes.c_int
-        lib.oracle_sgemm_rows.argtypes = [
-            _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
-            _i64, _vp, _vp, _vp, ctypes.c_int]
+        rows_args = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
+                     _i64, _vp, _vp, _vp, ctypes.c_int]
         lib.oracle_sgemm_rows_ex.restype = ctypes.c_int
-        lib.oracle_sgemm_rows_ex.argtypes = [ctypes.c_int, ctypes.c_int] + list(
-            lib.oracle_sgemm_rows.argtypes)
-        lib.oracle_sgemm.restype = ctypes.c_int
-        lib.oracle_sgemm.argtypes = [
-            _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
-            _vp, _vp, ctypes.c_int]
+        lib.oracle_sgemm_rows_ex.argtypes = [ctypes.c_int, ctypes.c_int] + rows_args
         lib.oracle_sum.restype = ctypes.c_int
         lib.oracle_sum.argtypes = [_i64, _vp, _vp, _vp]
-        lib.oracle_sgemm_points.restype = ctypes.c_int
-        lib.oracle_sgemm_points.argtypes = [
-            _i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
-            _i64, _vp, _vp, _vp, _vp, _vp]
+        points_args = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _f32, _vp, _i64,
+                       _i64, _vp, _vp, _vp, _vp, _vp]
         lib.oracle_sgemm_points_ex.restype = ctypes.c_int
-        lib.oracle_sgemm_points_ex.argtypes = [ctypes.c_int, ctypes.c_int] + list(
-            lib.oracle_sgemm_points.argtypes)
+        lib.oracle_sgemm_points_ex.argtypes = [ctypes.c_int, ctypes.c_int] + points_args
         self.lib = lib
 
     # -- whole matrix / selected rows ------------------------------------
@@ -123,7 +113,7 @@ class Oracle:
             m, n, k, alpha, _ptr(Af), lda, _ptr(Bf), ldb, beta, _ptr(Cout), ldc,
             nrows, _ptr(rows_arr), _ptr(S), _ptr(G), t)
         if rc != 0:
-            raise ValueError(f"oracle_sgemm_rows returned {rc}")
+            raise ValueError(f"oracle_sgemm_rows_ex returned {rc}")
         return {"C": Cout.reshape(np.shape(C)) if np.ndim(C) == 2 else Cout,
                 "S": S, "G": G}
 
@@ -159,7 +149,7 @@ class Oracle:
             m, n, k, alpha, _ptr(Af), lda, _ptr(Bf), ldb, beta, _ptr(Cf), ldc,
             ii.size, _ptr(ii), _ptr(jj), _ptr(out), _ptr(S), _ptr(G))
         if rc != 0:
-            raise ValueError(f"oracle_sgemm_points returned {rc}")
+            raise ValueError(f"oracle_sgemm_points_ex returned {rc}")
         return {"C": out, "S": S, "G": G}
 
 

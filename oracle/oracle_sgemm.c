@@ -176,27 +176,6 @@ int oracle_sgemm_rows_ex(int trans_a, int trans_b, int64_t m, int64_t n, int64_t
     return rc;
 }
 
-/* Operands as given (row-major A and B). */
-int oracle_sgemm_rows(int64_t m, int64_t n, int64_t k, float alpha,
-                      const float *A, int64_t lda, const float *B, int64_t ldb,
-                      float beta, float *C, int64_t ldc,
-                      int64_t nrows, const int64_t *rows,
-                      double *S, double *G, int nthreads)
-{
-    return oracle_sgemm_rows_ex(0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
-                                nrows, rows, S, G, nthreads);
-}
-
-/* Whole-matrix form: every row of C. */
-int oracle_sgemm(int64_t m, int64_t n, int64_t k, float alpha,
-                 const float *A, int64_t lda, const float *B, int64_t ldb,
-                 float beta, float *C, int64_t ldc,
-                 double *S, double *G, int nthreads)
-{
-    return oracle_sgemm_rows_ex(0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
-                                m, NULL, S, G, nthreads);
-}
-
 /*
  * oracle_sgemm_points_ex: single entries (ii[p], jj[p]) for p < npts,
  * computed as a dot product over ascending t -- the same sum, in the same
@@ -233,15 +212,4 @@ int oracle_sgemm_points_ex(int trans_a, int trans_b, int64_t m, int64_t n, int64
         if (G) G[p] = g;
     }
     return 0;
-}
-
-/* Operands as given (row-major A and B). */
-int oracle_sgemm_points(int64_t m, int64_t n, int64_t k, float alpha,
-                        const float *A, int64_t lda, const float *B, int64_t ldb,
-                        float beta, const float *C, int64_t ldc,
-                        int64_t npts, const int64_t *ii, const int64_t *jj,
-                        float *out, double *S, double *G)
-{
-    return oracle_sgemm_points_ex(0, 0, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
-                                  npts, ii, jj, out, S, G);
 }

@@ -43,3 +43,15 @@ def assert_exact(got, want, what=""):
         idx = np.argwhere(got != want)[:5]
         detail = ", ".join(f"{tuple(i)}: got {got[tuple(i)]!r} want {want[tuple(i)]!r}" for i in idx)
         raise AssertionError(f"{what}: {(got != want).sum()} entries differ; {detail}")
+
+
+def assert_close_blocked(got, want, G, alpha, beta, C_in, what="", block=1024):
+    """assert_close over row blocks of `block` rows (bounds the float64
+    temporaries of an 8192 x 8192 comparison); returns the largest err/tol."""
+    worst = 0.0
+    for r0 in range(0, np.shape(got)[0], block):
+        sl = slice(r0, r0 + block)
+        cin = C_in[sl] if beta != 0 else 0.0
+        worst = max(worst, assert_close(got[sl], want[sl], G[sl], alpha, beta, cin,
+                                        f"{what} rows {r0}.."))
+    return worst

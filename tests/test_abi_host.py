@@ -133,6 +133,34 @@ def test_splitk_argument_errors():
     assert f(0, 64, 1024, 1.0, None, 1024, None, 64, 0.0, None, 64, 0, None, 0) == E.SUCCESS
 
 
+def test_order_argument_errors():
+    E, f = hta, hta.mi_sgemm_with_order
+    assert f(-1, 2, 8, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4) == E.ERROR_INVALID_VALUE
+    assert f(-1, 1, 0, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4) == E.ERROR_INVALID_VALUE
+    assert f(99, 1, 8, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4) == E.ERROR_INVALID_VALUE
+    assert f(-1, 0, 1, 0, 0, 4, 4, 4, 1.0, P, 3, P, 4, 0.0, P, 4) == E.ERROR_INVALID_LD
+    assert f(-1, 0, 1, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4) == E.ERROR_DEVICE
+
+
+def test_splitk_combine_argument_errors():
+    """The combine entry checks sizes, ld, pointers and the slice layout (a
+    multiple of 4 floats, at least m*n rounded up to 4, 16-byte aligned
+    partials) before anything else."""
+    E, f = hta, hta.mi_sgemm_splitk_combine
+    assert f(-1, 4, 2, P, 16, 1.0, 0.0, P, 4) == E.ERROR_INVALID_VALUE
+    assert f(4, -1, 2, P, 16, 1.0, 0.0, P, 4) == E.ERROR_INVALID_VALUE
+    assert f(4, 4, -1, P, 16, 1.0, 0.0, P, 4) == E.ERROR_INVALID_VALUE
+    assert f(4, 4, 2, P, 16, 1.0, 0.0, P, 3) == E.ERROR_INVALID_LD
+    assert f(4, 4, 2, P, 16, 1.0, 0.0, None, 4) == E.ERROR_NULL_POINTER
+    assert f(4, 4, 2, None, 16, 1.0, 0.0, P, 4) == E.ERROR_NULL_POINTER
+    assert f(4, 4, 2, P, 18, 1.0, 0.0, P, 4) == E.ERROR_INVALID_VALUE   # slice % 4
+    assert f(5, 3, 2, P, 12, 1.0, 0.0, P, 3) == E.ERROR_INVALID_VALUE   # 15 > 12
+    assert f(4, 4, 2, P + 4, 16, 1.0, 0.0, P, 4) == E.ERROR_INVALID_VALUE   # unaligned
+    assert f(0, 4, 2, None, 0, 1.0, 0.0, None, 4) == E.SUCCESS
+    # a valid call reaches the device check (none here)
+    assert f(5, 3, 2, P, 16, 1.0, 0.0, P, 3) == E.ERROR_DEVICE
+
+
 def test_splitk_atomic_argument_errors():
     E, f = hta, hta.mi_sgemm_splitk_atomic
     assert f(-1, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4, 0) == E.ERROR_INVALID_VALUE

@@ -333,3 +333,22 @@ def test_splitk_combine_past_its_block_cap():
     assert_exact(got, exact_product(Ah[rows], Bh), "combine past its block cap")
     del A, B, C, C1
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("config", [-1, 0, 6, 9, 13, 14])
+def test_workgroup_order_is_bitwise_neutral(config):
+    """The workgroup order only decides which workgroup computes which tile:
+    every (XCD remap, group height) gives the bits of the default order,
+    including group heights that do not divide the tile rows."""
+    say("order", config)
+    m, n, k = 1000, 777, 333
+    rng = np.random.default_rng(21)
+    A = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).cuda()
+    B = torch.from_numpy(rng.standard_normal((k, n)).astype(np.float32)).cuda()
+    C0 = torch.from_numpy(rng.standard_normal((m, n)).astype(np.float32)).cuda()
+    cfg = None if config < 0 else config
+    ref = hta.sgemm(A, B, C0.clone(), 1.25, -0.5, config=cfg)
+    for order in [(1, 8), (0, 8), (1, 1), (0, 1), (0, 3), (1, 5), (1, 1000)]:
+        got = hta.sgemm(A, B, C0.clone(), 1.25, -0.5, config=cfg, order=order)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"order {order} config {config}"

@@ -3,15 +3,15 @@ oracle on the same seeded inputs.
 
 Bars: floating-point results within the tolerance in tests/parity.py; results
 on integer-valued operands bit-exact; padding of A and B (NaN) never read,
-padding of C (sentinel) never written.  At the full workload sizes the oracle
-computes sampled rows, and whole-matrix properties (row and column sums of an
-integer product, finiteness, untouched pads) cover every element.
+padding of C (sentinel) never written.  Every output element is compared, at
+the five workload sizes too: the oracle computes each full-size product once
+(float and integer twin) and every path is checked against it.
 """
 import numpy as np
 import pytest
 
 import synth
-from parity import assert_close, assert_exact
+from parity import assert_close, assert_close_blocked, assert_exact
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -95,31 +95,37 @@ def full_check(orc, kind, w, integer):
         assert_close(got, want, ref["G"], w.alpha, w.beta, C[:, :w.n], f"{kind} {w.name}")
 
 
-def sampled_check(orc, kind, w, integer, nrows, seed=0):
-    A, B, C = synth.operands(w, integer_twin=integer)
-    say(kind, w.name, "int" if integer else "float", f"rows={nrows}")
+# The oracle's product for one (workload, twin), kept for the tests that follow
+# (the paths of one workload run back to back); one entry at a time bounds the
+# host memory (an 8192^2 result with its G is 0.75 GiB).
+_REF = {}
+
+
+def reference(orc, w, integer):
+    """(A, B, C, oracle C over the logical m x n, G or None) of workload `w`."""
+    key = (w, integer)
+    if key not in _REF:
+        _REF.clear()
+        A, B, C = synth.operands(w, integer_twin=integer)
+        say("oracle", w.name, "int" if integer else "float")
+        ref = orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
+                        want_g=not integer)
+        want = np.ascontiguousarray(ref["C"].reshape(w.m, w.ldc)[:, :w.n])
+        _REF[key] = (A, B, C, want, ref["G"])
+    return _REF[key]
+
+
+def whole_check(orc, kind, w, integer):
+    """Every output element of `kind` on workload `w` against the oracle."""
+    A, B, C, want, G = reference(orc, w, integer)
+    say(kind, w.name, "int" if integer else "float", "all elements")
     out = gpu_gemm(kind, w, A, B, C)
     check_pads(out, C, w.n, kind)
-    rows = synth.sample_rows([w.wid, 99, seed], w.m, nrows)
-    ref = orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
-                    rows=rows, want_g=True)
-    want = ref["C"].reshape(w.m, w.ldc)[rows, :w.n]
-    got = out[rows, :w.n]
+    got = out[:, :w.n]
     if integer:
-        assert_exact(got, want, f"{kind} {w.name} int rows")
-        # every element: row sums and column sums of alpha*A*B + beta*C (exact
-        # in float64 for these integer inputs)
-        Ai = A[:, :w.k].astype(np.float64)
-        Bi = B[:, :w.n].astype(np.float64)
-        Ci = C[:, :w.n].astype(np.float64)
-        full = out[:, :w.n].astype(np.float64)
-        beta_term = w.beta * Ci if w.beta != 0 else 0.0
-        row_want = w.alpha * (Ai @ Bi.sum(axis=1)) + (beta_term.sum(axis=1) if w.beta != 0 else 0.0)
-        col_want = w.alpha * (Ai.sum(axis=0) @ Bi) + (beta_term.sum(axis=0) if w.beta != 0 else 0.0)
-        assert np.array_equal(full.sum(axis=1), row_want), "row sums"
-        assert np.array_equal(full.sum(axis=0), col_want), "column sums"
+        assert_exact(got, want, f"{kind} {w.name} int")
     else:
-        assert_close(got, want, ref["G"], w.alpha, w.beta, C[rows, :w.n], f"{kind} {w.name}")
+        assert_close_blocked(got, want, G, w.alpha, w.beta, C[:, :w.n], f"{kind} {w.name}")
     return out
 
 
@@ -150,31 +156,31 @@ def test_small_shapes(orc, kind, shape, ld_pad):
 @pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 def test_workload_256(orc, kind, integer):
-    full_check(orc, kind, synth.workload(0), integer)
+    whole_check(orc, kind, synth.workload(0), integer)
 
 
-@pytest.mark.parametrize("kind", ["mfma", "valu"])
+@pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 def test_workload_2048(orc, kind, integer):
-    sampled_check(orc, kind, synth.workload(1), integer, nrows=64)
+    whole_check(orc, kind, synth.workload(1), integer)
 
 
 @pytest.mark.parametrize("kind", ["mfma", "valu"])
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 def test_workload_8192_alpha_beta(orc, kind, integer):
-    sampled_check(orc, kind, synth.workload(2), integer, nrows=12)
+    whole_check(orc, kind, synth.workload(2), integer)
 
 
 @pytest.mark.parametrize("kind", ["mfma", "valu", "splitk"])
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 def test_workload_tails(orc, kind, integer):
-    sampled_check(orc, kind, synth.workload(3), integer, nrows=48)
+    whole_check(orc, kind, synth.workload(3), integer)
 
 
 @pytest.mark.parametrize("kind", ["splitk", "mfma", "splitk_atomic"])
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 def test_workload_splitk(orc, kind, integer):
-    sampled_check(orc, kind, synth.workload(4), integer, nrows=6)
+    whole_check(orc, kind, synth.workload(4), integer)
 
 
 # ---------------------------------------------------------------------------
@@ -244,15 +250,12 @@ def test_deterministic(kind):
 def test_splitk_matches_unsplit(orc):
     say("splitk vs unsplit")
     w = synth.workload(3)
-    A, B, C = synth.operands(w)
+    A, B, C, _, G = reference(orc, w, False)
     out_s = gpu_gemm("splitk", w, A, B, C)
     out_u = gpu_gemm("mfma", w, A, B, C)
-    rows = synth.sample_rows([3, 7], w.m, 8)
-    ref = orc.sgemm(w.m, w.n, w.k, w.alpha, A, w.lda, B, w.ldb, w.beta, C, w.ldc,
-                    rows=rows, want_g=True)
-    # both within tolerance of the oracle, and of each other (twice the bar)
-    G = ref["G"]
-    assert_close(out_s[rows, :w.n], out_u[rows, :w.n], 2 * G, 1.0, 0.0, 0.0, "split vs unsplit")
+    # within tolerance of each other (twice the bar), every element
+    assert_close_blocked(out_s[:, :w.n], out_u[:, :w.n], 2 * G, 1.0, 0.0, 0.0,
+                         "split vs unsplit")
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 5, 7, 64])
@@ -296,8 +299,8 @@ def test_splitk_atomic_beta_one_and_tolerance(orc):
     the atomic variant stay within the bar of the oracle."""
     say("splitk atomic beta=1")
     w = synth.workload(3).scaled(dist_c="uniform", alpha=-0.5, beta=1.0)
-    sampled_check(orc, "splitk_atomic", w, integer=False, nrows=16)
-    sampled_check(orc, "splitk_atomic", w, integer=True, nrows=16)
+    whole_check(orc, "splitk_atomic", w, integer=False)
+    whole_check(orc, "splitk_atomic", w, integer=True)
 
 
 # ---------------------------------------------------------------------------

@@ -189,3 +189,33 @@ def test_streamk_auto_one_per_cu(orc, shape):
     C2 = hta.sgemm_splitk(Afd, Bfd, splits=0)
     torch.cuda.synchronize()
     assert torch.equal(C1, C2)
+
+
+# The one-per-CU route on float operands, at and next to the ends of its k
+# range (the rule takes 1024 <= k <= 2048), with beta != 0 and one operand
+# stored transposed: every element within the tolerance of the oracle, and
+# the planner's choice asserted on each side of both ends.
+ONE_PER_CU_CASES = [(768, 768, k, ta) for k in (1023, 1024, 1025) for ta in (0, 1)] + \
+                   [(1536, 1536, k, ta) for k in (2047, 2048, 2049) for ta in (0, 1)]
+
+
+@pytest.mark.parametrize("case", ONE_PER_CU_CASES,
+                         ids=[f"{m}x{n}x{k}{'_tn' if ta else ''}" for m, n, k, ta in ONE_PER_CU_CASES])
+def test_streamk_one_per_cu_float_boundaries(orc, case):
+    m, n, k, ta = case
+    plan = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, m, n, k, 0)
+    one_per_cu = (plan["config"], plan["stream_k_grid"]) == (6, 256)
+    assert one_per_cu == (1024 <= k <= 2048), plan
+    w = synth.Workload(13, "skonef", m, n, k, k + 4, n + 4, n + 3, "uniform", "normal", 1.25, 0.5)
+    A, lda, B, ldb, C = synth.operands_ex(w, ta, 0)
+    say("one per CU float", m, n, k, "ta", ta, "plan", plan["config"], plan["stream_k_grid"])
+    Ad, Bd, Cd = (torch.from_numpy(x).cuda() for x in (A, B, C))
+    Av = Ad[:, :m].t() if ta else Ad[:, :k]
+    hta.sgemm_splitk(Av, Bd[:, :n], Cd[:, :n], w.alpha, w.beta, splits=0)
+    torch.cuda.synchronize()
+    out = Cd.cpu().numpy()
+    assert np.array_equal(out[:, n:], C[:, n:]), "C padding written"
+    ref = orc.sgemm(m, n, k, w.alpha, A, lda, B, ldb, w.beta, C, w.ldc, want_g=True,
+                    trans_a=bool(ta))
+    assert_close(out[:, :n], ref["C"].reshape(m, w.ldc)[:, :n], ref["G"], w.alpha, w.beta,
+                 C[:, :n], f"one per CU {m}x{n}x{k} ta={ta}")

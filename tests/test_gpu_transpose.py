@@ -138,31 +138,52 @@ def test_transposed_bitwise_equals_as_given(config):
 # ---------------------------------------------------------------------------
 # Workload sizes
 # ---------------------------------------------------------------------------
+# The as-given GPU result of one (kind, workload, twin), kept while the three
+# transposed forms of it are checked.
+_AS_GIVEN = {}
+
+
+def as_given(kind, w, integer):
+    key = (kind, w, integer)
+    if key not in _AS_GIVEN:
+        _AS_GIVEN.clear()
+        A, B, C = synth.operands(w, integer_twin=integer)
+        say(kind, w.name, "as given", "int" if integer else "float")
+        _AS_GIVEN[key] = gpu_gemm_ex(kind, w, 0, 0, A, B, C)
+    return _AS_GIVEN[key]
+
+
+def workload_check(orc, kind, w, combo, integer, nrows):
+    """Sampled rows against the oracle (its transposed-operand walk is
+    strided, so whole products at these sizes are slow), and every element
+    bitwise against the as-given call: the same tile configuration and plan
+    feed the matrix cores the same values in the same order."""
+    out = check(orc, kind, w, *combo, integer, rows=synth.sample_rows([w.wid, 98], w.m, nrows))
+    assert_exact(out, as_given(kind, w, integer), f"{kind} {w.name} ta,tb={combo} vs as given")
+
+
 @pytest.mark.parametrize("combo", COMBOS, ids=COMBO_IDS)
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 def test_workload_2048_transposed(orc, combo, integer):
-    w = synth.workload(1)
-    check(orc, "mfma", w, *combo, integer, rows=synth.sample_rows([w.wid, 98], w.m, 48))
+    workload_check(orc, "mfma", synth.workload(1), combo, integer, 48)
 
 
 @pytest.mark.parametrize("combo", COMBOS, ids=COMBO_IDS)
-def test_workload_8192_transposed(orc, combo):
-    w = synth.workload(2)
-    check(orc, "mfma", w, *combo, False, rows=synth.sample_rows([w.wid, 98], w.m, 8))
+@pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
+def test_workload_8192_transposed(orc, combo, integer):
+    workload_check(orc, "mfma", synth.workload(2), combo, integer, 8)
 
 
 @pytest.mark.parametrize("combo", COMBOS, ids=COMBO_IDS)
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 def test_workload_tails_transposed(orc, combo, integer):
-    w = synth.workload(3)
-    check(orc, "mfma", w, *combo, integer, rows=synth.sample_rows([w.wid, 98], w.m, 32))
+    workload_check(orc, "mfma", synth.workload(3), combo, integer, 32)
 
 
 @pytest.mark.parametrize("combo", COMBOS, ids=COMBO_IDS)
 @pytest.mark.parametrize("integer", [False, True], ids=["float", "int"])
 def test_workload_splitk_transposed(orc, combo, integer):
-    w = synth.workload(4)
-    check(orc, "splitk", w, *combo, integer, rows=synth.sample_rows([w.wid, 98], w.m, 4))
+    workload_check(orc, "splitk", synth.workload(4), combo, integer, 4)
 
 
 # ---------------------------------------------------------------------------
