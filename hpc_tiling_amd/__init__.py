@@ -23,7 +23,7 @@ __all__ = [
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
     "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex", "mi_sgemm_streamk",
     "mi_sgemm_streamk_workspace_bytes", "mi_sgemm_splitk_combine", "mi_clock_probe",
-    "mi_sgemm_with_order",
+    "mi_sgemm_with_order", "mi_sgemm_splitk_noalloc",
     "sgemm", "sgemm_streamk", "streamk_workspace", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace", "splitk_combine", "reduce_sum", "ClockProbe",
     "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "KERNEL_SPLITK_ATOMIC", "EXPORTED_SYMBOLS",
     "OP_N", "OP_T",
@@ -38,6 +38,8 @@ ERROR_NULL_POINTER = 3
 ERROR_WORKSPACE = 4
 ERROR_LAUNCH = 5
 ERROR_DEVICE = 6
+ERROR_SCRATCH_LIMIT = 7
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 KERNEL_MFMA = 0
 KERNEL_VALU = 1
@@ -54,7 +56,7 @@ EXPORTED_SYMBOLS = (
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
     "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex", "mi_sgemm_streamk",
     "mi_sgemm_streamk_workspace_bytes", "mi_sgemm_splitk_combine", "mi_clock_probe",
-    "mi_sgemm_with_order",
+    "mi_sgemm_with_order", "mi_sgemm_splitk_noalloc",
 )
 
 if not LIB_PATH.exists():
@@ -111,6 +113,8 @@ lib.mi_sgemm_splitk.argtypes = _GEMM_ARGS + [_i, _vp, _sz, _vp]
 lib.mi_sgemm_splitk.restype = _i
 lib.mi_sgemm_splitk_ex.argtypes = [_i, _i] + _GEMM_ARGS + [_i, _vp, _sz, _vp]
 lib.mi_sgemm_splitk_ex.restype = _i
+lib.mi_sgemm_splitk_noalloc.argtypes = [_i, _i] + _GEMM_ARGS + [_i, _vp]
+lib.mi_sgemm_splitk_noalloc.restype = _i
 lib.mi_sgemm_splitk_with_config.argtypes = [_i, _i, _i] + _GEMM_ARGS + [_i, _vp, _sz, _vp]
 lib.mi_sgemm_splitk_with_config.restype = _i
 lib.mi_sgemm_splitk_with_config_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
@@ -188,6 +192,12 @@ def mi_sgemm_splitk_ex(trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C
                        ws, ws_bytes, stream=None) -> int:
     return lib.mi_sgemm_splitk_ex(trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C,
                                   ldc, splits, ws, ws_bytes, stream)
+
+
+def mi_sgemm_splitk_noalloc(trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                            splits, stream=None) -> int:
+    return lib.mi_sgemm_splitk_noalloc(trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C,
+                                       ldc, splits, stream)
 
 
 def mi_sgemm_splitk_with_config(config, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta,

@@ -8,6 +8,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "mi_sgemm.h"
 #include "mfma_configs.hpp"
@@ -16,8 +17,36 @@
 #include "splitk.hpp"
 #include "clock.hpp"
 
+// Scratch of mi_sgemm_splitk_noalloc: the split-K partial sums (or stream-K
+// slots) of callers that cannot allocate device memory.  Each device the
+// library runs on holds its own copy until the process ends.  Host code never
+// uses this name as an address (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device
+// (mi::scratch_address).
+static __device__ __align__(256) float scratch[MI_SGEMM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
 namespace mi {
 namespace {
+
+constexpr size_t kScratchBytes = MI_SGEMM_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch is a whole number of 256-byte blocks");
+
+// The device address of `scratch` on the current device, looked up on the
+// first call for each device (with that device current) and kept; nullptr
+// when the runtime cannot give it.
+void *scratch_address() {
+    static std::mutex mu;
+    static void *addr[128] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 128) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
 
 // ---------------------------------------------------------------------------
 // Tile configurations of the matrix-core kernel (mfma_configs.hpp).
@@ -254,14 +283,15 @@ double sk_cost_us(int m, int n, const SplitPlan &sp, double efficiency,
 // the configuration is free) with the tiles mi_sgemm would choose.  Measured
 // on MI355X at 512 x 512 x 262144: 16 slices of the 128 x 128 x 32 tile, one
 // round of 256 workgroups.
-SplitPlan plan_split(int m, int n, int k, int splits, int config, bool allow_sk = true) {
+SplitPlan plan_split(int m, int n, int k, int splits, int config, bool allow_sk = true,
+                     size_t cap = kAutoWorkspaceCap) {
     if (m <= 0 || n <= 0 || k <= 0) return SplitPlan{config < 0 ? 0 : config, 0, 0, 0, 0};
     SplitPlan best{};
     double best_cost = 0.0;
     bool have = false;
     auto consider = [&](int id, long long want) {
         const SplitPlan sp = make_plan(m, n, k, want, id);
-        if (splits == 0 && sp.bytes > kAutoWorkspaceCap) return;
+        if (splits == 0 && sp.bytes > cap) return;
         const double cost = split_cost_us(m, n, sp, config_efficiency(id));
         if (!have || cost < best_cost * 0.99) {
             best = sp;
@@ -283,7 +313,7 @@ SplitPlan plan_split(int m, int n, int k, int splits, int config, bool allow_sk 
         // a tile's k steps (a shared tile then has at most about five parts)
         const SplitPlan sk = make_sk_plan(m, n, k, id, 0);
         if (allow_sk && 4 * (sk.sk_iters / sk.sk_grid) >= sk.sk_ksteps &&
-            sk.bytes <= kAutoWorkspaceCap) {
+            sk.bytes <= cap) {
             const double cost = sk_cost_us(m, n, sk, config_efficiency(id));
             if (cost < best_cost * 0.97) {
                 best = sk;
@@ -300,7 +330,7 @@ SplitPlan plan_split(int m, int n, int k, int splits, int config, bool allow_sk 
             k <= kStreamKOnePerCuMaxK) {
             const SplitPlan sk1 = make_sk_plan(m, n, k, id, kCUs);
             if (sk1.sk_grid > 0 && 4 * (sk1.sk_iters / sk1.sk_grid) >= sk1.sk_ksteps &&
-                sk1.bytes <= kAutoWorkspaceCap) {
+                sk1.bytes <= cap) {
                 const MfmaConfig &c1 = mfma_config(id);
                 const double seg = kWorkgroupOverheadUs * (double)(c1.bm * c1.bn) / (128.0 * 128.0);
                 // (discounted only against a single pass or slices: where the
@@ -510,9 +540,11 @@ int launch_streamk(const SplitPlan &sp, int ta, int tb, int m, int n, int k, flo
     return launch_raw(c.fixup, (long long)(sp.sk_workers - 1) * kFixupSplit, kFixupThreads, args, s);
 }
 
+// use_scratch: the workspace is the static scratch (ws ignored): the
+// automatic plan keeps within it, a forced plan beyond it is refused.
 int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, const float *A,
                int lda, const float *B, int ldb, float beta, float *C, int ldc, int splits,
-               void *ws, size_t ws_bytes, void *stream) {
+               void *ws, size_t ws_bytes, void *stream, bool use_scratch = false) {
     if (config >= kNumMfmaConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
     int st = check_sizes(m, n, k, lda, ldb, ldc, ta, tb);
     if (st) return st;
@@ -525,10 +557,19 @@ int run_splitk(int config, int ta, int tb, int m, int n, int k, float alpha, con
         st = check_device();
         return st ? st : launch_scale(m, n, beta, C, ldc, s);
     }
-    const SplitPlan sp = plan_split(m, n, k, splits, config);
-    if (sp.bytes > 0 && (!ws || ws_bytes < sp.bytes)) return MI_SGEMM_ERROR_WORKSPACE;
+    const SplitPlan sp =
+        plan_split(m, n, k, splits, config, true, use_scratch ? kScratchBytes : kAutoWorkspaceCap);
+    if (use_scratch) {
+        if (sp.bytes > kScratchBytes) return MI_SGEMM_ERROR_SCRATCH_LIMIT;
+    } else if (sp.bytes > 0 && (!ws || ws_bytes < sp.bytes)) {
+        return MI_SGEMM_ERROR_WORKSPACE;
+    }
     st = check_device();
     if (st) return st;
+    if (use_scratch && sp.bytes > 0) {
+        ws = scratch_address();
+        if (!ws) return MI_SGEMM_ERROR_LAUNCH;
+    }
     const int id = sp.config;
     if (sp.sk_grid > 0) return launch_streamk(sp, ta, tb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, ws, s);
     // one slice: the full-k kernel, no workspace (the same sums and rounding
@@ -698,6 +739,13 @@ int mi_sgemm_splitk_ex(int trans_a, int trans_b, int m, int n, int k, float alph
                       ws, ws_bytes, stream);
 }
 
+int mi_sgemm_splitk_noalloc(int trans_a, int trans_b, int m, int n, int k, float alpha,
+                            const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                            int ldc, int splits, void *stream) {
+    return run_splitk(-1, trans_a, trans_b, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                      nullptr, 0, stream, true);
+}
+
 int mi_sgemm_splitk_with_config(int config, int trans_a, int trans_b, int m, int n, int k,
                                 float alpha, const float *A, int lda, const float *B, int ldb,
                                 float beta, float *C, int ldc, int splits, void *ws,
@@ -821,6 +869,8 @@ const char *mi_status_string(int status) {
         case MI_SGEMM_ERROR_WORKSPACE: return "workspace missing or too small";
         case MI_SGEMM_ERROR_LAUNCH: return "kernel launch failed";
         case MI_SGEMM_ERROR_DEVICE: return "no current gfx950 device";
+        case MI_SGEMM_ERROR_SCRATCH_LIMIT:
+            return "the plan needs more than the 64 MiB static scratch of mi_sgemm_splitk_noalloc";
         default: return "unknown status";
     }
 }

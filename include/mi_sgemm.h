@@ -66,7 +66,9 @@ typedef enum mi_status {
     MI_SGEMM_ERROR_NULL_POINTER = 3,  /* NULL for an operand that would be read or written */
     MI_SGEMM_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than required */
     MI_SGEMM_ERROR_LAUNCH = 5,        /* the HIP runtime rejected a kernel launch */
-    MI_SGEMM_ERROR_DEVICE = 6         /* no current HIP device, or it is not gfx950 */
+    MI_SGEMM_ERROR_DEVICE = 6,        /* no current HIP device, or it is not gfx950 */
+    MI_SGEMM_ERROR_SCRATCH_LIMIT = 7  /* mi_sgemm_splitk_noalloc: the forced plan needs more
+                                         than MI_SGEMM_NOALLOC_SCRATCH_BYTES of scratch */
 } mi_status;
 
 /*
@@ -171,6 +173,35 @@ int mi_sgemm_splitk_ex(int trans_a, int trans_b, int m, int n, int k, float alph
                        const float *A, int lda, const float *B, int ldb,
                        float beta, float *C, int ldc,
                        int splits, void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of the static device scratch that mi_sgemm_splitk_noalloc uses. */
+#define MI_SGEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * mi_sgemm_splitk_noalloc -- mi_sgemm_splitk_ex for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same plans and kernels, with the
+ * workspace replaced by a static scratch buffer of
+ * MI_SGEMM_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each
+ * device it runs on until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine); the caller passes only the
+ * operands.  splits = 0: the automatic plan, kept within the scratch (a plan
+ * mi_sgemm_splitk_ex would run with more workspace is replaced by the best
+ * one that fits, down to the single-pass kernel; where the automatic plan of
+ * mi_sgemm_splitk_ex fits, it is the same plan and gives the same bits).  A
+ * forced split count whose plan needs more than the scratch returns
+ * MI_SGEMM_ERROR_SCRATCH_LIMIT before anything is enqueued.  Every call on one
+ * device shares that device's scratch (it keeps the last call's contents;
+ * nothing in it needs to start at zero): calls that overlap in time on one
+ * device -- on different streams, or from different host threads without
+ * ordering -- race and give wrong results; order them on one stream.  Other
+ * arguments, semantics and errors as mi_sgemm_splitk_ex (without
+ * MI_SGEMM_ERROR_WORKSPACE); a failure to obtain the scratch's device
+ * address gives MI_SGEMM_ERROR_LAUNCH.
+ */
+int mi_sgemm_splitk_noalloc(int trans_a, int trans_b, int m, int n, int k, float alpha,
+                            const float *A, int lda, const float *B, int ldb,
+                            float beta, float *C, int ldc, int splits, void *stream);
 
 /*
  * mi_sgemm_splitk_combine -- the second pass of mi_sgemm_splitk on its own:
