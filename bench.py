@@ -326,6 +326,36 @@ def combine_secondary(name="sgemm_splitk_512x512x262144", seconds=0.25):
     return res
 
 
+def valu_calibration(workgroups=256 * 32, iters=2000, launches=10):
+    """TFLOP/s of the two FMA loops of mi_fma_rate_probe (8 waves per SIMD):
+    the register outer product shaped like the VALU kernel's inner loop, and
+    FMA chains with scalar-register operands."""
+    import torch
+    import hpc_tiling_amd as hta
+    from hpc_tiling_amd import perfmodel as pm
+    out = torch.empty(256 * workgroups, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    res = {}
+    for loop, name, flop in ((0, "outer_product_8x8_vgpr", 136), (1, "chains_sgpr_operand", 256)):
+        launch = lambda: hta.mi_fma_rate_probe(loop, out.data_ptr(), workgroups, iters, s.cuda_stream)
+        for _ in range(3):
+            if launch() != hta.SUCCESS:
+                raise RuntimeError("mi_fma_rate_probe failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(launches):
+            launch()
+        e1.record(s)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / launches
+        tf = flop * iters * 256.0 * workgroups / sec / 1e12
+        res[name] = {"us_per_launch": 1e6 * sec, "tflops": tf,
+                     "frac_of_fp32_vector_peak": tf * 1e12 / pm.PEAK_FP32_VECTOR,
+                     "flop_per_launch": flop * iters * 256.0 * workgroups}
+    return res
+
+
 def reduce_secondary(name="reduce_sum_268435456", seconds=0.25):
     """The array sum on its largest workload: GB/s of algorithmic bytes (4n)
     and the fraction of the 8 TB/s HBM roofline."""
@@ -382,15 +412,20 @@ def summarize_counters(path, match, last):
     """Mean of every counter over the last `last` dispatches whose kernel name
     contains `match` in a rocprofv3 counter_collection.csv (--pmc)."""
     per_dispatch = {}
+    resources = {}
     for r in _rows(path):
         if match not in r["Kernel_Name"]:
             continue
         d = per_dispatch.setdefault(int(r["Dispatch_Id"]), {})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        resources = {k: r[k] for k in ("Kernel_Name", "Grid_Size", "Workgroup_Size", "VGPR_Count",
+                                       "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size",
+                                       "Scratch_Size") if k in r}
     ids = sorted(per_dispatch)
     sel = ids[-last:] if last else ids
     names = sorted({c for i in sel for c in per_dispatch[i]})
     return {"kernel_match": match, "dispatches_in_file": len(ids), "dispatches_used": len(sel),
+            "resources_of_last_dispatch": resources,
             "mean": {c: statistics.fmean(per_dispatch[i].get(c, 0.0) for i in sel)
                      for c in names}}
 
@@ -411,6 +446,8 @@ def main(argv=None):
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--reduce-only", action="store_true",
                     help="only time the array sum on its largest workload (for profiling)")
+    ap.add_argument("--valu-calibration", action="store_true",
+                    help="only time the FP32 FMA issue-rate probes (the VALU kernel's bound)")
     ap.add_argument("--combine-only", action="store_true",
                     help="only time the split-K combine kernel alone (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -454,6 +491,10 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
                           "launches": 5}), flush=True)
+        return 0
+
+    if args.valu_calibration:
+        print(json.dumps({"valu_calibration": valu_calibration()}), flush=True)
         return 0
 
     if args.reduce_only:

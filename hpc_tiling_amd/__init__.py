@@ -23,7 +23,7 @@ __all__ = [
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
     "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex", "mi_sgemm_streamk",
     "mi_sgemm_streamk_workspace_bytes", "mi_sgemm_splitk_combine", "mi_clock_probe",
-    "mi_sgemm_with_order", "mi_sgemm_splitk_noalloc",
+    "mi_sgemm_with_order", "mi_sgemm_splitk_noalloc", "mi_fma_rate_probe",
     "sgemm", "sgemm_streamk", "streamk_workspace", "sgemm_valu", "sgemm_splitk", "sgemm_splitk_atomic", "splitk_workspace", "splitk_combine", "reduce_sum", "ClockProbe",
     "KERNEL_MFMA", "KERNEL_VALU", "KERNEL_SPLITK", "KERNEL_SPLITK_ATOMIC", "EXPORTED_SYMBOLS",
     "OP_N", "OP_T",
@@ -56,7 +56,7 @@ EXPORTED_SYMBOLS = (
     "mi_sgemm_splitk_atomic", "mi_reduce_sum", "mi_reduce_sum_workspace_bytes",
     "mi_reduce_sum_max_additions", "mi_sgemm_ex", "mi_sgemm_splitk_ex", "mi_sgemm_streamk",
     "mi_sgemm_streamk_workspace_bytes", "mi_sgemm_splitk_combine", "mi_clock_probe",
-    "mi_sgemm_with_order", "mi_sgemm_splitk_noalloc",
+    "mi_sgemm_with_order", "mi_sgemm_splitk_noalloc", "mi_fma_rate_probe",
 )
 
 if not LIB_PATH.exists():
@@ -125,6 +125,8 @@ lib.mi_sgemm_streamk_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.mi_sgemm_streamk_workspace_bytes.restype = _sz
 lib.mi_sgemm_splitk_combine.argtypes = [_i, _i, _i, _vp, ctypes.c_longlong, _f, _f, _vp, _i, _vp]
 lib.mi_sgemm_splitk_combine.restype = _i
+lib.mi_fma_rate_probe.argtypes = [_i, _vp, _i, _i, _vp]
+lib.mi_fma_rate_probe.restype = _i
 lib.mi_clock_probe.argtypes = [_vp, _i, _i, ctypes.POINTER(_i), _vp]
 lib.mi_clock_probe.restype = _i
 lib.mi_sgemm_splitk_atomic.argtypes = _GEMM_ARGS + [_i, _vp]
@@ -228,6 +230,10 @@ def mi_sgemm_splitk_atomic(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, splits=
 
 def mi_sgemm_splitk_combine(m, n, splits, ws, slice, alpha, beta, C, ldc, stream=None) -> int:
     return lib.mi_sgemm_splitk_combine(m, n, splits, ws, slice, alpha, beta, C, ldc, stream)
+
+
+def mi_fma_rate_probe(loop, out, workgroups, iters, stream=None) -> int:
+    return lib.mi_fma_rate_probe(loop, out, workgroups, iters, stream)
 
 
 def mi_clock_probe(ticks, workgroups, spin_us, ref_khz, stream=None) -> int:

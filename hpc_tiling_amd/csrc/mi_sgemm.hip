@@ -16,6 +16,7 @@
 #include "reduce.hpp"
 #include "splitk.hpp"
 #include "clock.hpp"
+#include "fma_rate.hpp"
 
 // Scratch of mi_sgemm_splitk_noalloc: the split-K partial sums (or stream-K
 // slots) of callers that cannot allocate device memory.  Each device the
@@ -858,6 +859,24 @@ int mi_clock_probe(unsigned long long *ticks, int workgroups, int spin_us, int *
     void *args[] = {&ticks, &spin};
     return launch_raw(reinterpret_cast<const void *>(&clock_probe_kernel), workgroups, 64, args,
                       static_cast<hipStream_t>(stream));
+}
+
+int mi_fma_rate_probe(int loop, float *out, int workgroups, int iters, void *stream) {
+    if ((loop != kFmaOuter && loop != kFmaScalar) || workgroups < 1 || workgroups > 65536 ||
+        iters < 1 || iters > 1000000)
+        return MI_SGEMM_ERROR_INVALID_VALUE;
+    if (!out) return MI_SGEMM_ERROR_NULL_POINTER;
+    const int st = check_device();
+    if (st) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (loop == kFmaOuter) {
+        void *args[] = {&out, &iters};
+        return launch_raw(reinterpret_cast<const void *>(&fma_outer_kernel), workgroups, 256,
+                          args, s);
+    }
+    float a = 0.999f, b = 1e-3f;
+    void *args[] = {&out, &iters, &a, &b};
+    return launch_raw(reinterpret_cast<const void *>(&fma_scalar_kernel), workgroups, 256, args, s);
 }
 
 const char *mi_status_string(int status) {

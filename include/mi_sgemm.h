@@ -290,6 +290,25 @@ int mi_clock_probe(unsigned long long *ticks, int workgroups, int spin_us, int *
                    void *stream);
 
 /*
+ * mi_fma_rate_probe -- the issue rate of non-packed FP32 FMAs on the vector
+ * ALUs, the bound of mi_sgemm_valu (page aerisun.top, section
+ * "Register Tiling 与线程内复用", keeps the r_m x r_n outer product of the
+ * inner loop in registers).  `workgroups` workgroups of 256 threads each run
+ * `iters` iterations of one loop with no memory traffic:
+ *   loop 0: an 8 x 8 outer product of register values (64 v_fma_f32 with
+ *           every operand in a VGPR) plus 8 multiplies: 136 FLOP per thread
+ *           per iteration -- the shape of mi_sgemm_valu's inner loop;
+ *   loop 1: 16 independent chains x = x * a + b with a, b in scalar
+ *           registers, 8 rounds: 256 FLOP per thread per iteration.
+ * out: device memory for 256 * workgroups floats, written (one per thread,
+ * so the loops are not optimised away).  Time the launch with events and
+ * divide the FLOP count by it.  Errors: INVALID_VALUE (loop not 0 or 1,
+ * workgroups outside 1..65536, iters outside 1..10^6), NULL_POINTER,
+ * DEVICE, LAUNCH.
+ */
+int mi_fma_rate_probe(int loop, float *out, int workgroups, int iters, void *stream);
+
+/*
  * Text for a mi_status value (a static string; never NULL).  The statuses
  * report the preconditions that page "GPU 访存与计算优化" (aerisun.top),
  * section "float4 向量化的条件", states for a vectorised kernel -- sizes that

@@ -133,6 +133,23 @@ def test_splitk_argument_errors():
     assert f(0, 64, 1024, 1.0, None, 1024, None, 64, 0.0, None, 64, 0, None, 0) == E.SUCCESS
 
 
+def test_probe_argument_errors():
+    E = hta
+    f = hta.mi_fma_rate_probe
+    assert f(2, P, 1, 1) == E.ERROR_INVALID_VALUE
+    assert f(0, P, 0, 1) == E.ERROR_INVALID_VALUE
+    assert f(1, P, 1, 0) == E.ERROR_INVALID_VALUE
+    assert f(0, None, 1, 1) == E.ERROR_NULL_POINTER
+    assert f(0, P, 1, 1) == E.ERROR_DEVICE
+    ref = ctypes.c_int(0)
+    g = hta.mi_clock_probe
+    assert g(P, 0, 20, ref) == E.ERROR_INVALID_VALUE
+    assert g(P, 1025, 20, ref) == E.ERROR_INVALID_VALUE
+    assert g(P, 8, 0, ref) == E.ERROR_INVALID_VALUE
+    assert g(None, 8, 20, ref) == E.ERROR_NULL_POINTER
+    assert g(P, 8, 20, ref) == E.ERROR_DEVICE
+
+
 def test_order_argument_errors():
     E, f = hta, hta.mi_sgemm_with_order
     assert f(-1, 2, 8, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4) == E.ERROR_INVALID_VALUE

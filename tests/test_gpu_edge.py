@@ -352,3 +352,21 @@ def test_workgroup_order_is_bitwise_neutral(config):
         got = hta.sgemm(A, B, C0.clone(), 1.25, -0.5, config=cfg, order=order)
         torch.cuda.synchronize()
         assert torch.equal(got, ref), f"order {order} config {config}"
+
+
+def test_clock_and_fma_probes():
+    """The measurement helpers run and report plausible figures: a core clock
+    between 100 and 3000 MHz on every XCD, and finite outputs of both FMA
+    loops."""
+    say("probes")
+    probe = hta.ClockProbe()
+    probe.launch()
+    torch.cuda.synchronize()
+    mhz = probe.mhz()
+    assert len(mhz) == 8 and all(100 < x < 3000 for x in mhz), mhz
+    out = torch.full((256 * 64,), float("nan"), device="cuda")
+    for loop in (0, 1):
+        assert hta.mi_fma_rate_probe(loop, out.data_ptr(), 64, 10) == hta.SUCCESS
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        out.fill_(float("nan"))
