@@ -111,6 +111,11 @@ def make_step(kind, w, Av, Bv, Cv, ws):
     if kind.startswith("mfma_cfg"):
         cfg = int(kind[len("mfma_cfg"):])
         return lambda: hta.sgemm(Av, Bv, Cv, alpha, beta, config=cfg)
+    if kind.startswith("streamk_c"):
+        # forced stream-K schedule: streamk_c<config>_g<grid>
+        cfg, grid = (int(x) for x in kind[len("streamk_c"):].split("_g"))
+        return lambda: hta.sgemm_streamk(Av, Bv, Cv, alpha, beta, grid=grid, workspace=ws,
+                                         config=cfg)
     if kind.startswith("mfma_x"):
         # forced workgroup order: mfma_x<xcd_remap>g<group_m>, e.g. mfma_x0g1
         x, g = kind[len("mfma_x"):].split("g")
@@ -141,6 +146,9 @@ def setup(w, kind):
     ws = None
     if kind == "splitk":
         ws = hta.splitk_workspace(w.m, w.n, w.k, 0, device=dev)
+    elif kind.startswith("streamk_c"):
+        cfg, grid = (int(x) for x in kind[len("streamk_c"):].split("_g"))
+        ws = hta.streamk_workspace(w.m, w.n, w.k, grid, device=dev, config=cfg)
     torch.cuda.synchronize()
     return (A, B, C), (Ad, Bd, Cd), make_step(kind, w, Av, Bv, Cd[:, :w.n], ws)
 
@@ -258,7 +266,9 @@ def timed_calls(step, seconds):
     warm(step, 2, 0.02)
     probe, _ = time_trials(step, 2, 1)
     n = max(3, min(5000, int(seconds / max(probe[0] / 2, 1e-6))))
-    warm(step, 5, 0.1)
+    # (the operands of the next workload take seconds to generate, with the
+    # GPU idle: settle as long as for the headline)
+    warm(step, 5, SETTLE_S)
     secs, host = time_trials(step, n, 1)
     return n, secs[0] / n, host / n
 
@@ -439,8 +449,9 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--kernel", default="mfma",
                     help="mfma | valu | splitk | splitk_atomic | mfma_cfgN | mfma_x<0|1>g<G> "
-                         "(forced workgroup order); mfma and splitk take a suffix _nt, _tn "
-                         "or _tt for operands stored transposed")
+                         "(forced workgroup order) | streamk_c<config>_g<grid> (forced "
+                         "stream-K); mfma and splitk take a suffix _nt, _tn or _tt for "
+                         "operands stored transposed")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -515,6 +526,12 @@ def main(argv=None):
           file=sys.stderr, flush=True)
     import hpc_tiling_amd as hta
     probes = (hta.ClockProbe(), hta.ClockProbe())
+    # Launch the probe once now: its kernel is loaded on first use, and that
+    # host-side pause right before the timed steps would leave the GPU idle for
+    # milliseconds -- after such a pause the next ~100 ms of GEMM calls run up
+    # to 20 % slower on MI355X although the core clock reads normal.
+    for p in probes:
+        p.launch()
     extra_warmup = warm(step, args.warmup)
     secs, _ = time_trials(step, args.steps, args.trials, probes)
     sclk_before, sclk_after = (clock_summary(p.mhz()) for p in probes)
