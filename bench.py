@@ -111,6 +111,18 @@ def make_step(kind, w, Av, Bv, Cv, ws):
     if kind.startswith("mfma_cfg"):
         cfg = int(kind[len("mfma_cfg"):])
         return lambda: hta.sgemm(Av, Bv, Cv, alpha, beta, config=cfg)
+    if kind == "mfma_raw":
+        # the C entry point with its arguments prepared once: for products
+        # small enough that the Python helper's checks take longer than the
+        # kernel
+        import torch
+        (ta, tb, m, n, k, pa, lda, pb, ldb), C, pc, ldc, _ = hta._prepare_ex(Av, Bv, Cv, beta)
+        fn = hta.lib.mi_sgemm_ex
+        args = (ta, tb, m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
+                torch.cuda.current_stream().cuda_stream)
+        if fn(*args) != hta.SUCCESS:
+            raise RuntimeError("mi_sgemm_ex failed")
+        return lambda: fn(*args)
     if kind.startswith("streamk_c"):
         # forced stream-K schedule: streamk_c<config>_g<grid>
         cfg, grid = (int(x) for x in kind[len("streamk_c"):].split("_g"))
@@ -448,7 +460,8 @@ def main(argv=None):
     ap.add_argument("--trials", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--kernel", default="mfma",
-                    help="mfma | valu | splitk | splitk_atomic | mfma_cfgN | mfma_x<0|1>g<G> "
+                    help="mfma | mfma_raw (C entry, arguments prepared once) | valu | splitk | "
+                         "splitk_atomic | mfma_cfgN | mfma_x<0|1>g<G> "
                          "(forced workgroup order) | streamk_c<config>_g<grid> (forced "
                          "stream-K); mfma and splitk take a suffix _nt, _tn or _tt for "
                          "operands stored transposed")
@@ -600,7 +613,7 @@ def main(argv=None):
                  ("splitk", "sgemm_tails_3001x4997x1023"),
                  ("splitk", "sgemm_splitk_512x512x262144"),
                  ("splitk_atomic", "sgemm_splitk_512x512x262144"), ("valu", "sgemm_2048x2048x2048"),
-                 ("mfma", "sgemm_256x256x256"),
+                 ("mfma", "sgemm_256x256x256"), ("mfma_raw", "sgemm_256x256x256"),
                  ("mfma_nt", "sgemm_2048x2048x2048"), ("mfma_tn", "sgemm_2048x2048x2048"),
                  ("mfma_tt", "sgemm_2048x2048x2048"), ("mfma_tt", "sgemm_8192x8192x8192_ab"),
                  ("splitk_tn", "sgemm_splitk_512x512x262144"),

@@ -240,6 +240,43 @@ def test_graph_capture_replay():
         assert s.item() == float(x.cpu().double().sum()), f"graph replay {rep} reduce"
 
 
+def test_noalloc_entry_under_graph_capture():
+    """The allocation-free split-K entry (its partial sums in the library's
+    static scratch) captured into a graph -- the use it exists for -- and
+    replayed with new inputs between replays: every replay equals the
+    integer product, and equals the entry with a caller workspace."""
+    say("graph capture noalloc")
+    rng = np.random.default_rng(8)
+    m, n, k = 260, 190, 3000
+    A = torch.from_numpy(ints(rng, (m, k))).cuda()
+    B = torch.from_numpy(ints(rng, (k, n))).cuda()
+    C = torch.empty((m, n), device="cuda")
+    args = lambda stream: (0, 0, m, n, k, 1.0, A.data_ptr(), k, B.data_ptr(), n, 0.0,
+                           C.data_ptr(), n, 6, stream)
+    # the first call on the device sets the scratch up, outside capture
+    assert hta.mi_sgemm_splitk_noalloc(*args(torch.cuda.current_stream().cuda_stream)) == hta.SUCCESS
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            st = hta.mi_sgemm_splitk_noalloc(*args(side.cuda_stream))
+    assert st == hta.SUCCESS
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        A.copy_(torch.from_numpy(ints(rng, (m, k))).cuda())
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        assert_exact(got, exact_product(A.cpu().numpy(), B.cpu().numpy()), f"noalloc replay {rep}")
+        D = hta.sgemm_splitk(A, B, splits=6)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, D.cpu().numpy()), f"noalloc replay {rep} vs workspace entry"
+
+
 def test_concurrent_host_threads_and_streams():
     """Four host threads, each with its own stream and workspace, call the
     library at the same time (ctypes releases the GIL around each call); the
