@@ -2,7 +2,7 @@
  * abi_demo.c -- calls libmi_sgemm through its C ABI from plain C, with device
  * memory from the HIP runtime and no Python or torch in the process.
  *
- * It runs every compute entry point on small integer-valued operands (so the
+ * It runs the compute entry points on small integer-valued operands (so the
  * expected results are exact and are formed here with 64-bit integer sums),
  * checks a few argument errors, and prints "abi demo ok" on success; any
  * mismatch or error prints a line and gives exit status 1.
@@ -102,6 +102,21 @@ int main(void) {
     HIP_OK(hipStreamSynchronize(stream));
     HIP_OK(hipMemcpy(hC, C, sizeof(float) * m * n, hipMemcpyDeviceToHost));
     if (check("mi_sgemm_splitk", hC, want, m, n)) return 1;
+
+    /* the allocation-free split-K entry: no workspace argument, the same
+       result; a second call reuses the library's static scratch */
+    for (int rep = 0; rep < 2; ++rep) {
+        HIP_OK(hipMemset(C, 0, sizeof(float) * m * n));
+        st = mi_sgemm_splitk_noalloc(MI_SGEMM_OP_N, MI_SGEMM_OP_N, m, n, k, 1.f, A, k, B, n,
+                                     0.f, C, n, 3 + rep, stream);
+        if (st) return fail("mi_sgemm_splitk_noalloc", st);
+        HIP_OK(hipStreamSynchronize(stream));
+        HIP_OK(hipMemcpy(hC, C, sizeof(float) * m * n, hipMemcpyDeviceToHost));
+        if (check("mi_sgemm_splitk_noalloc", hC, want, m, n)) return 1;
+    }
+    if (mi_sgemm_splitk_noalloc(MI_SGEMM_OP_N, MI_SGEMM_OP_N, 2048, 2048, 4096, 1.f, A, 4096, B,
+                                2048, 0.f, C, 2048, 8, stream) != MI_SGEMM_ERROR_SCRATCH_LIMIT)
+        return fail("plan beyond the static scratch not rejected", -1);
 
     /* argument errors are reported before anything is enqueued */
     if (mi_sgemm(m, n, k, 1.f, A, k - 1, B, n, 0.f, C, n, stream) != MI_SGEMM_ERROR_INVALID_LD)

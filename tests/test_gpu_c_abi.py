@@ -1,8 +1,9 @@
 """The C ABI from plain C: tests/c_abi/abi_demo (built with gcc by
 hpc_tiling_amd/build.py) allocates device memory with the HIP runtime, calls
-mi_sgemm, mi_sgemm_ex (both operands transposed), mi_sgemm_splitk and
-mi_reduce_sum on integer-valued data, checks each result exactly against
-64-bit integer sums, and checks two argument errors.  It runs as a child
+mi_sgemm, mi_sgemm_ex (both operands transposed), mi_sgemm_splitk,
+mi_sgemm_splitk_noalloc (twice) and mi_reduce_sum on integer-valued data,
+checks each result exactly against 64-bit integer sums, and checks three
+argument errors.  It runs as a child
 process with no Python or torch inside."""
 import subprocess
 from pathlib import Path
