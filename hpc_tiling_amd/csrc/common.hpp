@@ -17,6 +17,11 @@ constexpr int kFull = 0, kPartial = 1, kAtomic = 2, kStreamK = 3;
 // by workgroup id.
 constexpr int kXcds = 8;
 
+// LDS that the resident workgroups of one CU can hold together: a little
+// under the CU's 160 KiB (measured: five workgroups of 32000 bytes run at
+// once on a CU, five of 32256 do not).
+constexpr long long kLdsPerCuBytes = 160000;
+
 // Everything a GEMM kernel needs; passed by value as the single kernel
 // argument.  Leading dimensions and slice strides are 64-bit so that row
 // offsets never overflow.

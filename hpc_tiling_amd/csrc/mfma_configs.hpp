@@ -70,8 +70,8 @@ template <> struct TileOf<10> { using type = MfmaTile<128, 128, 16, 2, 4, 2>; };
 template <> struct TileOf<11> { using type = MfmaTile<128, 128, 32, 4, 2, 2>; };
 // 64 x 64 x 16 built for six workgroups per CU
 template <> struct TileOf<12> { using type = MfmaTile<64, 64, 16, 2, 2, 3, 6>; };
-// the same tile with a four-buffer ring, five workgroups per CU
-template <> struct TileOf<13> { using type = MfmaTile<64, 64, 16, 2, 2, 4, 5>; };
+// the same tile with a four-buffer ring, four workgroups per CU
+template <> struct TileOf<13> { using type = MfmaTile<64, 64, 16, 2, 2, 4, 4>; };
 // 8 waves, two workgroups per CU, a four-buffer ring (64 KB of LDS each)
 template <> struct TileOf<14> { using type = MfmaTile<128, 128, 16, 4, 2, 4, 2>; };
 constexpr int kNumMfmaConfigs = 15;

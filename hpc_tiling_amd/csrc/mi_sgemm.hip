@@ -112,8 +112,8 @@ constexpr long long kTwoWorkgroupMinRounds = 3;
 constexpr int kSmallStepId = 12;
 constexpr long long kSmallStepMinRounds = 8;
 
-// The same tile with a four-buffer ring (id 13, five workgroups per CU; a
-// load then has nearly two k steps to land) wins once k is long enough to
+// The same tile with a four-buffer ring (id 13; four workgroups of 32 KiB
+// fit a CU's LDS; a load has nearly two k steps to land) wins once k is long enough to
 // pay for the deeper prologue: over k = 257 .. 4095 at 3000 x 5000,
 // 2500 x 6000 and 8000^2 it lost 1-4 % up to k = 777 and won 0.5-2 % from
 // k = 900 on (3000 x 5000 x 1023: 123.5 -> 125.0, x 2047: 127.9 -> 130.5;
@@ -210,12 +210,17 @@ double config_efficiency(int id) {
 }
 
 // Workgroups of configuration `config` one CU holds at once (LDS, wave
-// slots, and the register budget the kernel was built for).
+// slots, and the register budget the kernel was built for).  The LDS the
+// workgroups of one CU may hold together is a little under the 160 KiB the
+// CU has (kLdsPerCuBytes): probed on MI355X with workgroups of a given LDS
+// size, five of 32000 bytes ran together on a CU but only four of 32256
+// (three of 53248, two of 54272), while hipOccupancyMaxActiveBlocksPerMultiprocessor
+// reported five and three.
 long long resident_per_cu(int config) {
     const MfmaConfig &c = mfma_config(config);
     const long long lds = (long long)c.stages * (c.bm * c.bk + c.bk * c.bn) * 4;
     const long long waves = (long long)c.wgm * c.wgn;
-    long long r = (160LL * 1024) / lds;
+    long long r = kLdsPerCuBytes / lds;
     if (r > 32 / waves) r = 32 / waves;
     if (c.max_wgs > 0 && r > c.max_wgs) r = c.max_wgs;
     return r < 1 ? 1 : r;

@@ -75,7 +75,8 @@ struct MfmaTile {
     static constexpr int LDS_BYTES = STAGES * (BM * BK + BK * BN) * 4;
     static_assert(GROUPS % 2 == 0, "fragment double-buffering needs an even group count");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one workgroup");
+    static_assert(LDS_BYTES <= kLdsPerCuBytes, "LDS budget of one workgroup");
+    static_assert(WGS * LDS_BYTES <= kLdsPerCuBytes, "WGS workgroups must fit one CU's LDS");
     static_assert(STAGES >= 2 && STAGES <= 4, "ring of two to four buffers");
 };
 
@@ -639,10 +640,66 @@ void sgemm_mfma_kernel(GemmArgs p) {
             }
         }
     };
+    // Tiles that lie inside the output (most of them) take a lean path:
+    // `corner` is the tile's first element, each lane adds one 32-bit byte
+    // offset and each accumulator register a row offset the whole wave shares,
+    // with no bounds checks, 64-bit index products or branches per element.
+    // The checked path costs about 15 instructions per element; on the
+    // ragged-tail shape (four 64 x 64 workgroups per CU) its epilogue took
+    // about 14 us while the other workgroups kept the matrix cores busy, a
+    // quarter of each workgroup's lifetime spent holding its slot.  Byte
+    // offsets stay below 2^32 when BM * ld < 2^30.
+    auto lean_ok = [&](int ld) {
+        return m0 + T::BM <= p.m && n0 + T::BN <= p.n && (long long)T::BM * ld < (1ll << 30);
+    };
+    // `block(addr, v)` gets each 32 x 32 block's registers v and addr(r), the
+    // address of register r's element.
+    auto for_each_lean = [&](float *corner, int ld, auto block) {
+        const unsigned lane_off = (unsigned)((wm * T::WTM + 4 * lh) * ld + wn * T::WTN + li);
+#pragma unroll
+        for (int a = 0; a < T::FM; ++a) {
+#pragma unroll
+            for (int b = 0; b < T::FN; ++b) {
+                auto addr = [&](int r) {
+                    const unsigned e =
+                        lane_off + (unsigned)((32 * a + 8 * (r >> 2) + (r & 3)) * ld + 32 * b);
+                    return reinterpret_cast<float *>(reinterpret_cast<char *>(corner) + 4u * e);
+                };
+                block(addr, acc[a][b]);
+            }
+        }
+    };
+    auto store_lean = [&](float *corner, int ld) {
+        for_each_lean(corner, ld, [&](auto addr, const f32x16 &v) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) *addr(r) = v[r];
+        });
+    };
     // C = alpha * acc + beta * C.  C is touched once: nontemporal access
     // (measured about 1 % faster at 2048^3 and 8192^3, probably less dirty L2
     // to write back when the kernel ends).
     auto store_c = [&]() {
+        if (lean_ok(p.ldc)) {
+            float *corner = p.C + (long long)m0 * p.ldc + n0;
+            if (p.beta == 0.f) {
+                for_each_lean(corner, p.ldc, [&](auto addr, const f32x16 &v) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(p.alpha * v[r], addr(r));
+                });
+            } else {
+                // a block's 16 loads in flight together, then its stores
+                for_each_lean(corner, p.ldc, [&](auto addr, const f32x16 &v) {
+                    float c[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) c[r] = __builtin_nontemporal_load(addr(r));
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        __builtin_nontemporal_store(__builtin_fmaf(p.beta, c[r], p.alpha * v[r]),
+                                                    addr(r));
+                });
+            }
+            return;
+        }
         for_each_output([&](int row, int col, float v) {
             float *dst = p.C + (long long)row * p.ldc + col;
             float r = p.alpha * v;
@@ -686,10 +743,10 @@ void sgemm_mfma_kernel(GemmArgs p) {
             if (ks == 0 && ke == p.sk_ksteps) {
                 store_c();
             } else {
+                // (the whole slot is written; entries outside C are never
+                // stored by the fixup)
                 float *slot = p.ws + (w * 2 + (ks > 0 ? 0 : 1)) * (long long)(T::BM * T::BN);
-                for_each_output([&](int row, int col, float v) {
-                    slot[(row - m0) * T::BN + (col - n0)] = v;
-                });
+                store_lean(slot, T::BN);
             }
             it += ke - ks;
         }
@@ -710,9 +767,14 @@ void sgemm_mfma_kernel(GemmArgs p) {
             // next finds them in cache.  At 512 x 512 x 262144 (16 slices) the
             // combine took 4.82 us after ordinary stores against 5.24 us after
             // nontemporal ones, with the partial kernel unchanged (932 us).
-            for_each_output([&](int row, int col, float v) {
-                p.ws[(long long)slice * p.ws_slice + (long long)row * p.n + col] = v;
-            });
+            if (lean_ok(p.n)) {
+                float *corner = p.ws + (long long)slice * p.ws_slice + (long long)m0 * p.n + n0;
+                store_lean(corner, p.n);
+            } else {
+                for_each_output([&](int row, int col, float v) {
+                    p.ws[(long long)slice * p.ws_slice + (long long)row * p.n + col] = v;
+                });
+            }
         } else if constexpr (MODE == kAtomic) {
             for_each_output([&](int row, int col, float v) {
                 unsafeAtomicAdd(p.C + (long long)row * p.ldc + col, p.alpha * v);

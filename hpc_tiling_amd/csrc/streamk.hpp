@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kFixupThreads) void streamk_fixup_kernel(
     // ... of the tile (row-major, BN a multiple of 4).  The parts are added in
     // order, the loads of PG parts in flight together (a tile is usually
     // shared by two or three workgroups: one round trip to memory).  Entries
-    // of the slots outside C's extent were never written and are not stored.
+    // of the slots outside C's extent are added like the others but never
+    // stored.
     constexpr int BAND = BM * BN / 4 / kFixupSplit;
     constexpr int PER = BAND / kFixupThreads;
     static_assert(PER >= 1 && BAND % kFixupThreads == 0, "a band must fill the block");

@@ -303,7 +303,7 @@ def test_tile_choice_rules():
     one or two rounds, the 8-wave 128 x 128 x 16 tile for two workgroups per
     CU from 3 rounds of 128 x 128 tiles, 64 x 64 x 32 where it quantises better, and 64 x 64 x 16
     (six workgroups per CU) when k leaves a partial 32-wide step on 8 or more
-    rounds of 64 x 64 tiles, in its four-buffer form (five per CU) from
+    rounds of 64 x 64 tiles, in its four-buffer form (four per CU) from
     k = 848 on."""
     def tile(m, n, k):
         p = hta.mi_sgemm_get_plan(hta.KERNEL_MFMA, -1, m, n, k, 0)

@@ -294,6 +294,45 @@ def test_non_default_stream():
     assert torch.equal(D, torch.full((m, n), float(k), device="cuda"))
 
 
+def test_side_stream_allocations_not_reused_early():
+    """stream= a side stream that is not torch's current one, with C and the
+    workspace left to the helpers: they are allocated for the side stream, so
+    the current stream's allocations and writes made while the kernels still
+    run cannot land in them.  Integer-valued operands: exact results."""
+    say("side stream, helper-allocated C and workspaces")
+    rng = np.random.default_rng(21)
+    m, n, k = 512, 512, 65536
+    Ah, Bh = rng.integers(-3, 4, (m, k)).astype(np.float32), rng.integers(-3, 4, (k, n)).astype(np.float32)
+    want = (Ah.astype(np.int64) @ Bh.astype(np.int64)).astype(np.float32)
+    xh = rng.integers(-3, 4, 1 << 22).astype(np.float32)
+    A, B, x = torch.from_numpy(Ah).cuda(), torch.from_numpy(Bh).cuda(), torch.from_numpy(xh).cuda()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        # the side stream waits for nothing, so its kernels run while the
+        # current stream allocates and overwrites memory below
+        outs.append(("splitk", hta.sgemm_splitk(A, B, splits=16, stream=side)))
+        outs.append(("streamk", hta.sgemm_streamk(A[:, :4096], B[:4096], stream=side)))
+        outs.append(("sgemm", hta.sgemm(A[:, :2048], B[:2048], stream=side)))
+        outs.append(("sum", hta.reduce_sum(x, stream=side)))
+        junk = [torch.full((1 << 20,) if i % 2 else (m * n * 17,), float("nan"), device="cuda")
+                for i in range(8)]
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    want_k = {
+        "splitk": want,
+        "streamk": (Ah[:, :4096].astype(np.int64) @ Bh[:4096].astype(np.int64)).astype(np.float32),
+        "sgemm": (Ah[:, :2048].astype(np.int64) @ Bh[:2048].astype(np.int64)).astype(np.float32),
+    }
+    for name, got in outs:
+        if name == "sum":
+            assert float(got.item()) == float(xh.astype(np.int64).sum()), "side-stream reduce_sum"
+        else:
+            assert_exact(got.cpu().numpy(), want_k[name], f"side-stream {name}")
+
+
 def test_splitk_atomic_beta_one_and_tolerance(orc):
     """beta == 1 skips the scaling pass (C accumulates in place); results of
     the atomic variant stay within the bar of the oracle."""
