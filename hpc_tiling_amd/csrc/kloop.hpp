@@ -4,10 +4,11 @@
 //
 // The tile of step s goes to LDS ring buffer s % NS (NS = 2 to 4 buffers) and
 // is loaded D = NS - 1 steps ahead: the prologue loads steps 0 .. D-1, step s
-// loads step s + D.  A load is direct (global -> LDS, whole k steps only:
-// step index < ndirect) or staged through VGPRs (the partial last k step, or
-// every step when direct loads cannot address the operands).  The steps run
-// in three phases, each with its loads fixed at compile time where possible:
+// loads step s + D.  A load is direct (global -> LDS: the whole k steps,
+// index < ndirect, and the partial last k step with its k tail masked) or
+// staged through VGPRs (every step when direct loads cannot address the
+// operands).  The steps run in three phases, each with its loads fixed at
+// compile time where possible:
 //   steady   [0, steady_end)           NS steps per iteration, every load
 //                                      direct (each ring position a constant);
 //   decided  [steady_end, auto_end)    NS steps per iteration, each step
@@ -21,7 +22,11 @@
 
 namespace mi {
 
-// What a step loads for the step D ahead.
+// What a step loads for the step D ahead.  kLoadRegs is the partial last k
+// step (or any step when direct loads are off); on four-buffer rings with
+// direct loads on it is loaded directly too, four bytes per lane, with the
+// elements past the end of k sent out of the buffer's range (they land in LDS
+// as zeros).
 constexpr int kLoadNone = 0, kLoadDirect = 1, kLoadRegs = 2, kLoadAuto = 3;
 
 constexpr int kTailMax = 5;       // steps left after the loops, at most
@@ -33,6 +38,28 @@ constexpr int kTailDecided = -1;  // tail: every remaining step decides its load
 // step s the tile t = s + D.
 constexpr int load_of(int t, int nsteps, int ndirect) {
     return t >= nsteps ? kLoadNone : (t < ndirect ? kLoadDirect : kLoadRegs);
+}
+
+// Whether the partial last k step is loaded directly (with `direct_ok`: the
+// operands are addressable by direct loads): only on four-buffer rings, where
+// its load can stay in flight across the barrier of the step that issues it;
+// on shorter rings that barrier waits for the load either way, and staging it
+// through VGPRs costs fewer registers.
+constexpr bool partial_step_direct(int ns, bool direct_ok) { return ns == 4 && direct_ok; }
+
+// Whether a load of kind `load` goes straight to LDS (no VGPR staging):
+// whole steps always, the partial step when `direct_on`
+// (partial_step_direct).
+constexpr bool loads_directly(int load, bool direct_on) {
+    return load == kLoadDirect || (load == kLoadRegs && direct_on);
+}
+
+// Whether the barrier that ends a step may leave the load that step issued
+// in flight: only on four-buffer rings, whose loads run three steps ahead,
+// and only for loads that go straight to LDS (a staged tile is written to
+// LDS from VGPRs before the barrier, so its load is complete by then).
+constexpr bool keeps_load_in_flight(int ns, int load, bool direct_on) {
+    return ns == 4 && loads_directly(load, direct_on);
 }
 
 // The fixed tail sequences: r remaining steps, the first nd of them whole.

@@ -140,6 +140,12 @@ struct Operand {
         return KROWS ? (int)(4 * ((long long)r * ld + min(col, e_last)))
                      : (int)(4 * ((long long)min(r, e_last) * ld + col));
     }
+    // k index, within its step, of word w of the swizzled LDS tile (the word
+    // word_offset(w, ...) loads).
+    __device__ static int word_k(int w) {
+        const int r = w / ROW_WORDS, u = w % ROW_WORDS;
+        return KROWS ? r : 4 * ((u >> 2) ^ swz(r)) + (u & 3);
+    }
     // Direct loads need every byte offset of a tile to fit the 31-bit range.
     __device__ static bool direct_fits(long long ld) {
         return ld < (1LL << 31) / (4LL * (KROWS ? T::BK : E));
@@ -189,6 +195,10 @@ struct Operand {
 // Word 3 of a raw (untyped) buffer resource on gfx9-class parts: 32-bit data
 // format, no swizzling; with stride 0 the range check is a byte count.
 constexpr int kBufferWord3 = 0x00020000;
+
+// A lane offset past the 2^31 - 1 bytes every buffer resource here covers:
+// the load is out of range, reads nothing and returns zero.
+constexpr int kOutOfRange = (int)0x80000000u;
 
 __device__ __forceinline__ __attribute__((address_space(3))) void *lds_ptr(float *p) {
     return (__attribute__((address_space(3))) void *)p;
@@ -362,6 +372,36 @@ void sgemm_mfma_kernel(GemmArgs p) {
         }
     };
 
+    // The partial last k step, directly as well: four bytes per lane (a
+    // 16-byte chunk may straddle the end of k), the words whose k lies past
+    // the end given an offset out of the buffer's range, so that they land in
+    // LDS as zeros (both operands: a NaN in a pad must not meet a zero).  The
+    // words go where the swizzled layout puts them, as in the 4-byte loads of
+    // unaligned operands; m / n edges are clamped the same way.
+    auto load_direct_masked = [&](int step, auto buf) {
+        float *as = a_buf(buf), *bs = b_buf(buf);
+        const float *abase = OA::tile_base(Ablk, p.lda, step * T::BK);
+        const float *bbase = OB::tile_base(Bblk, p.ldb, step * T::BK);
+        const int kv = kend - kbeg - step * T::BK;  // k values left in this step
+        const int a_last = min(T::BM, p.m - m0) - 1, b_last = min(T::BN, p.n - n0) - 1;
+        // (computed here, once per tile: kept from being hoisted to the
+        // kernel's start, where the offsets would hold registers throughout)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int i = 0; i < OA::PER4; ++i) {
+            const int win = i * T::WAVES + wave, w = win * 64 + ln;
+            load_lds4(abase, as + win * 64,
+                      OA::word_k(w) < kv ? OA::word_offset(w, p.lda, a_last) : kOutOfRange);
+        }
+#pragma unroll
+        for (int i = 0; i < OB::PER4; ++i) {
+            const int win = i * T::WAVES + wave, w = win * 64 + ln;
+            load_lds4(bbase, bs + win * 64,
+                      OB::word_k(w) < kv ? OB::word_offset(w, p.ldb, b_last) : kOutOfRange);
+        }
+    };
+
     // ---- masked loads through VGPRs (edges, k tail, unaligned) -------------
     struct Stage {
         f32x4 a[OA::PER], b[OB::PER];
@@ -459,22 +499,28 @@ void sgemm_mfma_kernel(GemmArgs p) {
     if (nsteps > 0) {
         set_frag_addr();
         Frag f[2];
+        // Stream-K runs a four-buffer tile as a three-buffer ring: its
+        // segments restart the pipeline mid-kernel, and the deeper ring
+        // measured slower there.
+        constexpr int NS = MODE == kStreamK && T::STAGES > 3 ? 3 : T::STAGES, D = NS - 1;
+        // direct loads one wave issues per step (a whole step; the partial one)
+        constexpr int DIRECT_LOADS = VEC ? OA::PER + OB::PER : OA::PER4 + OB::PER4;
+        constexpr int MASKED_LOADS = OA::PER4 + OB::PER4;
+        // the partial last k step goes straight to LDS too (four buffers)
+        const bool direct_on = partial_step_direct(NS, direct_ok);
         // load the tile of one of the first D steps
         auto fill = [&](int step, auto buf) {
-            if (load_of(step, nsteps, ndirect) == kLoadDirect) {
+            const int load = load_of(step, nsteps, ndirect);
+            if (load == kLoadDirect) {
                 load_direct(step, buf);
+            } else if (loads_directly(load, direct_on)) {
+                load_direct_masked(step, buf);
             } else {
                 Stage st;
                 load_regs(st, step);
                 store_regs(st, buf);
             }
         };
-        // Stream-K runs a four-buffer tile as a three-buffer ring: its
-        // segments restart the pipeline mid-kernel, and the deeper ring
-        // measured slower there.
-        constexpr int NS = MODE == kStreamK && T::STAGES > 3 ? 3 : T::STAGES, D = NS - 1;
-        // direct loads one wave issues per step
-        constexpr int DIRECT_LOADS = VEC ? OA::PER + OB::PER : OA::PER4 + OB::PER4;
         fill(0, S0{});
         if (D >= 2 && nsteps > 1) fill(1, S1{});
         if (D >= 3 && nsteps > 2) fill(2, std::integral_constant<int, 2>{});
@@ -509,16 +555,24 @@ void sgemm_mfma_kernel(GemmArgs p) {
             const int load = LOAD == kLoadAuto ? load_of(step + D, nsteps, ndirect) : LOAD;
             const bool ahead = load != kLoadNone;
             const bool direct = load == kLoadDirect;
+            const bool masked = load == kLoadRegs && direct_on;  // partial step, directly
+            const bool staged = ahead && !direct && !masked;
+            auto issue = [&]() {
+                if (direct)
+                    load_direct(step + D, WRT{});
+                else if (masked)
+                    load_direct_masked(step + D, WRT{});
+            };
             Stage st;
-            if (!direct && ahead) load_regs(st, step + D);
-            if (LOAD_GROUP == 0 && direct) load_direct(step + D, WRT{});
+            if (staged) load_regs(st, step + D);
+            if (LOAD_GROUP == 0) issue();
             // The fences keep the scheduler from sinking the loads and the
             // next group's LDS reads below the MFMAs that hide them.
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int g = 0; g < T::GROUPS; ++g) {
-                if (g > 0 && g == LOAD_GROUP && direct) {
-                    load_direct(step + D, WRT{});
+                if (g > 0 && g == LOAD_GROUP && (direct || masked)) {
+                    issue();
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 // (the last step reads the next buffer too: stale, unused, and
@@ -532,12 +586,14 @@ void sgemm_mfma_kernel(GemmArgs p) {
                 mfma_group(f[g & 1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (!direct && ahead) store_regs(st, WRT{});
+            if (staged) store_regs(st, WRT{});
             // Four buffers: the loads just issued (for step + 3) keep running
             // across the barrier; the ones issued a step earlier (step + 2)
             // must be complete, in every wave, before it.
-            if (NS == 4 && direct)
+            if (keeps_load_in_flight(NS, load, direct_on) && direct)
                 barrier_keep_newest<DIRECT_LOADS>();
+            else if (keeps_load_in_flight(NS, load, direct_on))
+                barrier_keep_newest<MASKED_LOADS>();
             else
                 __syncthreads();
             // two buffers: step + 1's tile is complete only after the barrier

@@ -4,9 +4,11 @@ tests/kloop/kloop_sim.cpp replays the kernel's loop over the k steps of a
 tile (prologue, steady loop, deciding loop, fixed or decided tail) with the
 schedule functions the kernel includes (hpc_tiling_amd/csrc/kloop.hpp), for
 1 to 64 steps on rings of 2 to 4 buffers, with direct loads off, every step
-whole, or a partial last step.  It checks that every step runs exactly once
-on its ring position, every tile is loaded once (directly exactly when it is
-a whole k step), and no tile is read before a barrier has waited for it.
+whole, or a partial last step (loaded directly with its k tail masked when
+direct loads are on).  It checks that every step runs exactly once on its
+ring position, every tile is loaded once (directly when it is a whole k step,
+or the partial step with direct loads on), and no tile is read before a
+barrier has waited for it.
 
 The replay is pinned by mistakes planted in copies of the header: each one
 must make it fail.  "alias_negative_whole_steps" is the kind of key aliasing
@@ -37,6 +39,10 @@ MUTANTS = [
     ("direct_partial_step", "(t < ndirect ? kLoadDirect : kLoadRegs)",
      "(t <= ndirect ? kLoadDirect : kLoadRegs)"),
     ("load_one_past_end", "return t >= nsteps ? kLoadNone", "return t > nsteps ? kLoadNone"),
+    ("masked_load_with_direct_off", "return load == kLoadDirect || (load == kLoadRegs && direct_on);",
+     "return load == kLoadDirect || load == kLoadRegs;"),
+    ("in_flight_on_three_buffers", "return ns == 4 && loads_directly(load, direct_on);",
+     "return ns >= 3 && loads_directly(load, direct_on);"),
 ]
 
 
