@@ -301,8 +301,9 @@ void sgemm_mfma_kernel(GemmArgs p) {
         else return Bs3;
     };
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    // (not const: the stream-K segment loop launders them, see there)
+    int tid = threadIdx.x;
+    int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / T::WGN, wn = wave % T::WGN;
 
@@ -442,12 +443,7 @@ void sgemm_mfma_kernel(GemmArgs p) {
                 for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
     };
 
-    const int li = lane & 31, lh = lane >> 5;
-    int a_off[T::FM], a_sw[T::FM], b_off[T::FN], b_sw[T::FN];
-#pragma unroll
-    for (int a = 0; a < T::FM; ++a) OA::frag_setup(wm * T::WTM + 32 * a, li, lh, a_off[a], a_sw[a]);
-#pragma unroll
-    for (int b = 0; b < T::FN; ++b) OB::frag_setup(wn * T::WTN + 32 * b, li, lh, b_off[b], b_sw[b]);
+    int li = lane & 31, lh = lane >> 5;
 
     struct Frag {
         typename OA::Frag a[T::FM];
@@ -460,6 +456,11 @@ void sgemm_mfma_kernel(GemmArgs p) {
     // registers for the epilogue.
     int a_addr[T::FM][T::GROUPS], b_addr[T::FN][T::GROUPS];
     auto set_frag_addr = [&]() {
+        int a_off[T::FM], a_sw[T::FM], b_off[T::FN], b_sw[T::FN];
+#pragma unroll
+        for (int a = 0; a < T::FM; ++a) OA::frag_setup(wm * T::WTM + 32 * a, li, lh, a_off[a], a_sw[a]);
+#pragma unroll
+        for (int b = 0; b < T::FN; ++b) OB::frag_setup(wn * T::WTN + 32 * b, li, lh, b_off[b], b_sw[b]);
 #pragma unroll
         for (int g = 0; g < T::GROUPS; ++g) {
 #pragma unroll
@@ -790,6 +791,12 @@ void sgemm_mfma_kernel(GemmArgs p) {
             tile0 = dp;
         }
         while (it < end) {
+            // Per-lane indices pass through an empty asm statement at the top
+            // of each segment, so that addresses derived from them are
+            // computed per segment instead of being hoisted out of the loop
+            // and held in registers across every k step (which made this
+            // instance spill).
+            asm volatile("" : "+v"(tid), "+v"(lane), "+v"(li), "+v"(lh));
             const long long t = it / p.sk_ksteps;
             const int ks = (int)(it - t * p.sk_ksteps);
             const int ke = (int)min((long long)p.sk_ksteps, ks + (end - it));
