@@ -17,10 +17,17 @@ constexpr int kFull = 0, kPartial = 1, kAtomic = 2, kStreamK = 3;
 // by workgroup id.
 constexpr int kXcds = 8;
 
-// LDS that the resident workgroups of one CU can hold together: a little
-// under the CU's 160 KiB (measured: five workgroups of 32000 bytes run at
-// once on a CU, five of 32256 do not).
-constexpr long long kLdsPerCuBytes = 160000;
+// LDS is handed to workgroups in granules of 1280 bytes, 128 per CU (its
+// 160 KiB).  Probed on MI355X with workgroups of a given LDS size, the
+// workgroups that ran on one CU at once were floor(128 / granules) for every
+// size tried from 24 to 54 KiB: five of 32000 bytes (25 granules) but four of
+// 32256 or 32768 (26), four of 40960 (32), three of 53248 (42), two of 54272
+// (43).
+constexpr int kLdsGranuleBytes = 1280;
+constexpr int kLdsGranulesPerCu = 128;
+constexpr int lds_granules(long long bytes) {
+    return (int)((bytes + kLdsGranuleBytes - 1) / kLdsGranuleBytes);
+}
 
 // Everything a GEMM kernel needs; passed by value as the single kernel
 // argument.  Leading dimensions and slice strides are 64-bit so that row

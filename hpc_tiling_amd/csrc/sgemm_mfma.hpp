@@ -75,8 +75,8 @@ struct MfmaTile {
     static constexpr int LDS_BYTES = STAGES * (BM * BK + BK * BN) * 4;
     static_assert(GROUPS % 2 == 0, "fragment double-buffering needs an even group count");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(LDS_BYTES <= kLdsPerCuBytes, "LDS budget of one workgroup");
-    static_assert(WGS * LDS_BYTES <= kLdsPerCuBytes, "WGS workgroups must fit one CU's LDS");
+    static_assert(WGS * lds_granules(LDS_BYTES) <= kLdsGranulesPerCu,
+                  "WGS workgroups must fit one CU's LDS");
     static_assert(STAGES >= 2 && STAGES <= 4, "ring of two to four buffers");
 };
 
