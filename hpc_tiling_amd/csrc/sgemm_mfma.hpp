@@ -77,6 +77,8 @@ struct MfmaTile {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(WGS * lds_granules(LDS_BYTES) <= kLdsGranulesPerCu,
                   "WGS workgroups must fit one CU's LDS");
+    // the LDS holds only one workgroup per CU
+    static constexpr bool ONE_PER_CU = 2 * lds_granules(LDS_BYTES) > kLdsGranulesPerCu;
     static_assert(STAGES >= 2 && STAGES <= 4, "ring of two to four buffers");
 };
 
@@ -697,14 +699,11 @@ void sgemm_mfma_kernel(GemmArgs p) {
             }
         }
     };
-    // Tiles that lie inside the output (most of them) take a lean path:
+    // Tiles that lie inside the output (most of them) can take a lean path:
     // `corner` is the tile's first element, each lane adds one 32-bit byte
     // offset and each accumulator register a row offset the whole wave shares,
-    // with no bounds checks, 64-bit index products or branches per element.
-    // The checked path costs about 15 instructions per element; on the
-    // ragged-tail shape (four 64 x 64 workgroups per CU) its epilogue took
-    // about 14 us while the other workgroups kept the matrix cores busy, a
-    // quarter of each workgroup's lifetime spent holding its slot.  Byte
+    // with no bounds checks, 64-bit index products or branches per element
+    // (the checked path costs about 15 instructions per element).  Byte
     // offsets stay below 2^32 when BM * ld < 2^30.
     auto lean_ok = [&](int ld) {
         return m0 + T::BM <= p.m && n0 + T::BN <= p.n && (long long)T::BM * ld < (1ll << 30);
@@ -734,9 +733,13 @@ void sgemm_mfma_kernel(GemmArgs p) {
     };
     // C = alpha * acc + beta * C.  C is touched once: nontemporal access
     // (measured about 1 % faster at 2048^3 and 8192^3, probably less dirty L2
-    // to write back when the kernel ends).
+    // to write back when the kernel ends).  The lean path is for tiles of
+    // which a CU holds several workgroups, whose epilogues overlap the
+    // others' matrix work (ragged-tail shape +2 %, 8192^3 with beta +1 %);
+    // with one 16-wave workgroup per CU the checked path measured 0.4 %
+    // faster at 2048^3 (four pairs of runs back to back).
     auto store_c = [&]() {
-        if (lean_ok(p.ldc)) {
+        if (!T::ONE_PER_CU && lean_ok(p.ldc)) {
             float *corner = p.C + (long long)m0 * p.ldc + n0;
             if (p.beta == 0.f) {
                 for_each_lean(corner, p.ldc, [&](auto addr, const f32x16 &v) {
