@@ -15,6 +15,8 @@ from parity import assert_close, assert_exact
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
+from storage import stored_device  # noqa: E402
+
 if torch.cuda.is_available():
     import hpc_tiling_amd as hta
     N_CFG = hta.mi_sgemm_config_count(hta.KERNEL_MFMA)
@@ -29,20 +31,6 @@ CASES = 1000
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-
-
-def stored_device(values, trans, pad, offset):
-    """Device storage of a logical operand: itself or its transpose, rows
-    padded by `pad` floats (NaN), the whole block starting `offset` floats
-    into its allocation.  Returns (keep-alive tensor, logical view, ld)."""
-    S = np.ascontiguousarray(values.T) if trans else values
-    rows, cols = S.shape
-    ld = cols + pad
-    flat = torch.full((offset + rows * ld + 4,), float("nan"), device="cuda")
-    blk = flat[offset:offset + rows * ld].view(rows, ld)
-    blk[:, :cols] = torch.from_numpy(S).cuda()
-    view = blk[:, :cols]
-    return flat, (view.t() if trans else view), ld
 
 
 @pytest.mark.parametrize("case", range(CASES))
