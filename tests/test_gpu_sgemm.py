@@ -303,7 +303,9 @@ def test_side_stream_allocations_not_reused_early():
     rng = np.random.default_rng(21)
     m, n, k = 512, 512, 65536
     Ah, Bh = rng.integers(-3, 4, (m, k)).astype(np.float32), rng.integers(-3, 4, (k, n)).astype(np.float32)
-    want = (Ah.astype(np.int64) @ Bh.astype(np.int64)).astype(np.float32)
+    # Exact in float64 (integer products and partial sums below 9k < 2^53),
+    # and a BLAS product: numpy's int64 product takes minutes at this size.
+    want = (Ah.astype(np.float64) @ Bh.astype(np.float64)).astype(np.float32)
     xh = rng.integers(-3, 4, 1 << 22).astype(np.float32)
     A, B, x = torch.from_numpy(Ah).cuda(), torch.from_numpy(Bh).cuda(), torch.from_numpy(xh).cuda()
     side = torch.cuda.Stream()
@@ -323,8 +325,8 @@ def test_side_stream_allocations_not_reused_early():
     torch.cuda.synchronize()
     want_k = {
         "splitk": want,
-        "streamk": (Ah[:, :4096].astype(np.int64) @ Bh[:4096].astype(np.int64)).astype(np.float32),
-        "sgemm": (Ah[:, :2048].astype(np.int64) @ Bh[:2048].astype(np.int64)).astype(np.float32),
+        "streamk": (Ah[:, :4096].astype(np.float64) @ Bh[:4096].astype(np.float64)).astype(np.float32),
+        "sgemm": (Ah[:, :2048].astype(np.float64) @ Bh[:2048].astype(np.float64)).astype(np.float32),
     }
     for name, got in outs:
         if name == "sum":
