@@ -438,14 +438,18 @@ def sgemm(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None, order=Non
     return C
 
 
-def sgemm_valu(A, B, C=None, alpha=1.0, beta=0.0, stream=None):
+def sgemm_valu(A, B, C=None, alpha=1.0, beta=0.0, stream=None, config=None):
     """Same as sgemm (row-major operands only), on the register-tiled VALU
-    kernel."""
+    kernel; `config` forces its configuration (0: one k group, 1: two)."""
     dev = _tensor_device(A, "A")
     with _current(dev), _on_stream(stream, dev):
         m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _prepare(A, B, C, beta)
-        st = lib.mi_sgemm_valu(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc,
-                               _stream(None, dev))
+        s = _stream(None, dev)
+        if config is None:
+            st = lib.mi_sgemm_valu(m, n, k, alpha, pa, lda, pb, ldb, beta, pc, ldc, s)
+        else:
+            st = lib.mi_sgemm_with_config(KERNEL_VALU, config, 0, 0, m, n, k, alpha, pa, lda,
+                                          pb, ldb, beta, pc, ldc, s)
     if st != SUCCESS:
         raise MiSgemmError(st, "mi_sgemm_valu")
     return C

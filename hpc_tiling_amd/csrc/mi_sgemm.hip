@@ -505,9 +505,23 @@ int run_mfma(int config, int ta, int tb, int m, int n, int k, float alpha, const
     return launch_full(id, ta, tb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, order);
 }
 
+// VALU configurations: 0 the 256-thread tile of the worked example, 1 the
+// same tile with two k groups (512 threads; see sgemm_valu.hpp).  Two k
+// groups win when each CU gets at most one workgroup (back to back on one
+// MI355X, TFLOP/s, 256 -> 512 threads: 2048^3 57.5 -> 77.6, 1024^2 x 8192
+// 14.8 -> 23.3); with more tiles the 256-thread tile puts two workgroups on
+// a CU and wins (4096^3 91.7 -> 87.9, 8192^3 88.0 -> 82.0).  Without 16-byte
+// loads the two-group instance spills (the element loads need more
+// registers), so it is not chosen there.
+constexpr int kNumValuConfigs = 2;
+constexpr long long kValuKGroupMaxTiles = 256;
+int choose_valu_config(long long tiles, bool vec) {
+    return vec && tiles <= kValuKGroupMaxTiles ? 1 : 0;
+}
+
 int run_valu(int config, int m, int n, int k, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
-    if (config > 0) return MI_SGEMM_ERROR_INVALID_VALUE;
+    if (config >= kNumValuConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     bool done;
     int st = prologue(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, &done);
@@ -516,8 +530,11 @@ int run_valu(int config, int m, int n, int k, float alpha, const float *A, int l
     a.tiles_m = (int)ceil_div(m, ValuTile::BM);
     a.tiles_n = (int)ceil_div(n, ValuTile::BN);
     const long long grid = (long long)a.tiles_m * a.tiles_n;
-    KernelFn fn = vector_ok(A, lda, B, ldb) ? &sgemm_valu_kernel<true> : &sgemm_valu_kernel<false>;
-    return launch(fn, grid, ValuTile::NT, s, a);
+    const bool vec = vector_ok(A, lda, B, ldb);
+    const int id = config < 0 ? choose_valu_config(grid, vec) : config;
+    KernelFn fn = id == 1 ? (vec ? &sgemm_valu_kernel<true, 2> : &sgemm_valu_kernel<false, 2>)
+                          : (vec ? &sgemm_valu_kernel<true, 1> : &sgemm_valu_kernel<false, 1>);
+    return launch(fn, grid, ValuTile::NT * (id == 1 ? 2 : 1), s, a);
 }
 
 // Stream-K: the persistent-grid kernel, then the fixup of shared tiles.
@@ -900,7 +917,7 @@ const char *mi_status_string(int status) {
 
 int mi_sgemm_config_count(int kernel) {
     if (kernel == MI_SGEMM_KERNEL_MFMA) return kNumMfmaConfigs;
-    if (kernel == MI_SGEMM_KERNEL_VALU) return 1;
+    if (kernel == MI_SGEMM_KERNEL_VALU) return kNumValuConfigs;
     if (kernel == MI_SGEMM_KERNEL_SPLITK || kernel == MI_SGEMM_KERNEL_SPLITK_ATOMIC)
         return kNumMfmaConfigs;
     return 0;
@@ -917,11 +934,12 @@ int mi_sgemm_get_plan(int kernel, int config, int m, int n, int k, int splits,
     plan->k_per_split = k;
     long long sk_workgroups = 0;
     if (kernel == MI_SGEMM_KERNEL_VALU) {
-        if (config > 0) return MI_SGEMM_ERROR_INVALID_VALUE;
-        plan->config = 0;
+        if (config >= kNumValuConfigs) return MI_SGEMM_ERROR_INVALID_VALUE;
+        const long long tiles = ceil_div(m, ValuTile::BM) * ceil_div(n, ValuTile::BN);
+        plan->config = config < 0 ? choose_valu_config(tiles, true) : config;
         plan->tile_m = ValuTile::BM; plan->tile_n = ValuTile::BN; plan->tile_k = ValuTile::BK;
         plan->micro_m = ValuTile::RM; plan->micro_n = ValuTile::RN;
-        plan->threads = ValuTile::NT;
+        plan->threads = ValuTile::NT * (plan->config == 1 ? 2 : 1);
         plan->small_iterations = ValuTile::BK;
         plan->fma_per_small_iteration = ValuTile::RM * ValuTile::RN;
         plan->outputs_per_thread = ValuTile::RM * ValuTile::RN;

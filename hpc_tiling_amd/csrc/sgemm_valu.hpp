@@ -23,9 +23,9 @@
 //     "gemm优化", section on prefetch, with one more step of distance): the
 //     tile of step t+2 is loaded before the FMAs of step t, and the tile of
 //     step t+1 (loaded a step earlier) goes to the other LDS buffer after
-//     them.  At 2048^3 each SIMD holds a single wave of this kernel, so the
-//     load latency must fit in the FMAs of a step or more: one step (2048
-//     FMA cycles) was not enough.
+//     them.  With one k group (below) at 2048^3 each SIMD holds a single
+//     wave of this kernel, so the load latency must fit in the FMAs of a
+//     step or more: one step (2048 FMA cycles) was not enough.
 #pragma once
 
 #include <type_traits>
@@ -36,23 +36,40 @@ namespace mi {
 
 struct ValuTile {
     static constexpr int BM = 128, BN = 128, BK = 8, RM = 8, RN = 8;
-    static constexpr int NT = (BM / RM) * (BN / RN);  // 256
+    static constexpr int NT = (BM / RM) * (BN / RN);  // 256 threads per k group
     static constexpr int LDS_S = 128 + 8;
+    static constexpr int STAGE = BK * LDS_S;           // floats of one A or B stage
 };
 
-template <bool VEC>
-__global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
+// KG k groups of 256 threads share a tile: group g takes the k steps
+// g, g + KG, g + 2 KG, ... with LDS buffers of its own, and at the end group 0
+// adds the other groups' sums, in group order, through LDS.  With KG = 2 a
+// CU's one workgroup of a one-round grid has two waves per SIMD, so that one
+// wave's LDS waits and barriers are covered by the other's FMAs.
+template <bool VEC, int KG>
+__global__ __launch_bounds__(256 * KG) void sgemm_valu_kernel(GemmArgs p) {
     using T = ValuTile;
-    __shared__ __attribute__((aligned(16))) float As[2][T::BK * T::LDS_S];
-    __shared__ __attribute__((aligned(16))) float Bs[2][T::BK * T::LDS_S];
+    // KG groups x two buffers x (A, B) stages; with KG > 1 the same memory
+    // later holds the sums of groups 1 .. KG-1 (64 per thread).
+    constexpr int STAGES_F = KG * 2 * 2 * T::STAGE;
+    constexpr int XCH_F = (KG - 1) * T::RM * T::RN * T::NT;
+    __shared__ __attribute__((aligned(16))) float smem[STAGES_F > XCH_F ? STAGES_F : XCH_F];
 
-    const int tid = threadIdx.x;
+    const int g = KG > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / T::NT) : 0;
+    const int tid = (int)threadIdx.x % T::NT;
     const int tx = tid & 15, ty = tid >> 4;
+    // buffer b of the group: its A stage, then its B stage
+    auto As = [&](int b) { return smem + (g * 2 + b) * 2 * T::STAGE; };
+    auto Bs = [&](int b) { return smem + (g * 2 + b) * 2 * T::STAGE + T::STAGE; };
 
     int tm, tn;
     grouped_tile(xcd_contiguous(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     const int nsteps = (p.k + T::BK - 1) / T::BK;
+    // every group runs the same number of steps (and barriers); steps past
+    // the end load zeros
+    const int nloc = (nsteps + KG - 1) / KG;
+    auto gstep = [&](int j) { return KG * j + g; };
     const bool full_m = m0 + T::BM <= p.m;
     const bool full_n = n0 + T::BN <= p.n;
 
@@ -91,8 +108,8 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
     };
     auto store_step = [&](const Regs &r, int buf) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) As[buf][(ac + c) * T::LDS_S + ar] = r.a[c];
-        *reinterpret_cast<f32x4 *>(&Bs[buf][br * T::LDS_S + bc]) = r.b;
+        for (int c = 0; c < 4; ++c) As(buf)[(ac + c) * T::LDS_S + ar] = r.a[c];
+        *reinterpret_cast<f32x4 *>(Bs(buf) + br * T::LDS_S + bc) = r.b;
     };
 
     float acc[T::RM][T::RN];
@@ -101,9 +118,9 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < T::RN; ++j) acc[i][j] = 0.f;
 
-    if (nsteps > 0) {
-        load_step(r0, 0);
-        if (nsteps > 1) load_step(r1, 1);
+    if (nloc > 0) {
+        load_step(r0, gstep(0));
+        if (nloc > 1) load_step(r1, gstep(1));
         store_step(r0, 0);
         __syncthreads();
     }
@@ -117,8 +134,8 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
         f32x4 a0, a1, b0, b1;
     };
     auto read_frag = [&](Frag &f, int buf, int kk) {
-        const float *arow = &As[buf][kk * T::LDS_S];
-        const float *brow = &Bs[buf][kk * T::LDS_S];
+        const float *arow = As(buf) + kk * T::LDS_S;
+        const float *brow = Bs(buf) + kk * T::LDS_S;
         f.a0 = *reinterpret_cast<const f32x4 *>(arow + 4 * ty);
         f.a1 = *reinterpret_cast<const f32x4 *>(arow + 64 + 4 * ty);
         f.b0 = *reinterpret_cast<const f32x4 *>(brow + 4 * tx);
@@ -134,13 +151,14 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
     };
     // FULL: the steady state of an interior tile (the tile of step+2 exists
     // and is whole), without any branch in the step.
+    // `step` counts the group's own steps (global step gstep(step)).
     auto one_step = [&](int step, Regs &cur, Regs &nxt, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int buf = step & 1;
         if (FULL)
-            load_full(cur, step + 2);
-        else if (step + 2 < nsteps)
-            load_step(cur, step + 2);
+            load_full(cur, gstep(step + 2));
+        else if (step + 2 < nloc)
+            load_step(cur, gstep(step + 2));
         Frag f[2];
         read_frag(f[0], buf, 0);
 #pragma unroll
@@ -150,24 +168,48 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
             fma_block(f[kk & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (FULL || step + 1 < nsteps) store_step(nxt, buf ^ 1);
+        if (FULL || step + 1 < nloc) store_step(nxt, buf ^ 1);
         __syncthreads();
     };
     // Two steps per iteration, so the register sets alternate at compile
-    // time; the steady loop stops while the tile four steps ahead is whole.
+    // time; the steady loop stops while the group's tile three steps ahead
+    // is whole.
     int step = 0;
     if (VEC && full_m && full_n) {
         const int nfull = p.k / T::BK;
-        for (; step + 3 < nfull; step += 2) {
+        for (; gstep(step + 3) < nfull; step += 2) {
             one_step(step, r0, r1, std::true_type{});
             one_step(step + 1, r1, r0, std::true_type{});
         }
     }
-    for (; step + 1 < nsteps; step += 2) {
+    for (; step + 1 < nloc; step += 2) {
         one_step(step, r0, r1, std::false_type{});
         one_step(step + 1, r1, r0, std::false_type{});
     }
-    if (step < nsteps) one_step(step, r0, r1, std::false_type{});
+    if (step < nloc) one_step(step, r0, r1, std::false_type{});
+
+    if constexpr (KG > 1) {
+        // The last step ended with a barrier: no wave reads a stage any more.
+        // Value (i, j) of thread t of group q sits at (q-1, i, j, t): a wave
+        // writes and reads 64 consecutive floats.
+        float *xch = smem;
+        if (g > 0) {
+#pragma unroll
+            for (int i = 0; i < T::RM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::RN; ++j)
+                    xch[(((g - 1) * T::RM + i) * T::RN + j) * T::NT + tid] = acc[i][j];
+        }
+        __syncthreads();
+        if (g > 0) return;
+#pragma unroll
+        for (int q = 1; q < KG; ++q)
+#pragma unroll
+            for (int i = 0; i < T::RM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::RN; ++j)
+                    acc[i][j] += xch[(((q - 1) * T::RM + i) * T::RN + j) * T::NT + tid];
+    }
 
     // Epilogue: row i of the micro tile is C row m0 + 4ty + i (i < 4) or
     // m0 + 64 + 4ty + i - 4; columns likewise with tx.

@@ -115,8 +115,13 @@ int mi_sgemm_ex(int trans_a, int trans_b, int m, int n, int k, float alpha,
  * 一个具体的例子: 128 x 128 workgroup tiles, k step 8, 256 threads each owning
  * an 8 x 8 block of C updated by outer products of 8 A and 8 B values
  * (page aerisun.top, section "Register Tiling 与线程内复用"), with a
- * double-buffered LDS stage.  Same arguments, semantics and errors as
- * mi_sgemm.  It is bound by the FP32 vector peak (non-packed FMA).
+ * double-buffered LDS stage.  When every CU gets at most one tile (at most
+ * 256 tiles) and A and B allow 16-byte loads, two such groups of 256 threads
+ * share a tile (512 threads per workgroup), each taking every other k step,
+ * and the first adds the second's sums before the store (a fixed order, so
+ * results are reproducible); VALU configuration ids: 0 one group, 1 two.
+ * Same arguments, semantics and errors as mi_sgemm.  It is bound by the
+ * FP32 vector peak (non-packed FMA).
  */
 int mi_sgemm_valu(int m, int n, int k, float alpha,
                   const float *A, int lda, const float *B, int ldb,

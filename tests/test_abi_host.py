@@ -51,13 +51,27 @@ def test_status_strings():
 
 def test_valu_plan_is_the_worked_example():
     g = {k: int(v) for k, v in _golden("worked_example_2048.txt").items()}
-    p = hta.mi_sgemm_get_plan(hta.KERNEL_VALU, -1, g["m"], g["n"], g["k"])
+    p = hta.mi_sgemm_get_plan(hta.KERNEL_VALU, 0, g["m"], g["n"], g["k"])
     for key in ("tile_m", "tile_n", "tile_k", "micro_m", "micro_n", "workgroups", "threads",
                 "outputs_per_thread", "big_iterations", "small_iterations",
                 "fma_per_small_iteration", "a_elements_per_big_iteration",
                 "b_elements_per_big_iteration"):
         assert p[key] == g[key], key
     assert p["tile_m"] * p["tile_n"] == g["c_elements_per_block"]
+
+
+def test_valu_automatic_k_groups():
+    """The automatic VALU plan splits each tile over two k groups while no CU
+    gets a second workgroup (at most 256 tiles), and keeps the worked
+    example's 256 threads otherwise."""
+    assert hta.mi_sgemm_config_count(hta.KERNEL_VALU) == 2
+    for (m, n, k, cfg, threads) in [(2048, 2048, 2048, 1, 512), (256, 256, 256, 1, 512),
+                                    (2048, 2049, 64, 0, 256), (4096, 4096, 4096, 0, 256),
+                                    (128 * 16, 128 * 16, 7, 1, 512), (128 * 16 + 1, 128 * 16, 7, 0, 256)]:
+        p = hta.mi_sgemm_get_plan(hta.KERNEL_VALU, -1, m, n, k)
+        assert (p["config"], p["threads"]) == (cfg, threads), (m, n, k)
+        assert p["workgroups"] == -(-m // 128) * -(-n // 128)
+    assert hta.mi_sgemm_get_plan(hta.KERNEL_VALU, 1, 4096, 4096, 8)["threads"] == 512
 
 
 def test_mfma_plan_geometry():
@@ -196,7 +210,8 @@ def test_with_config_rejects_unknown_ids():
     assert n >= 1
     r = hta.mi_sgemm_with_config(hta.KERNEL_MFMA, n, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
     assert r == hta.ERROR_INVALID_VALUE
-    r = hta.mi_sgemm_with_config(hta.KERNEL_VALU, 1, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    nv = hta.mi_sgemm_config_count(hta.KERNEL_VALU)
+    r = hta.mi_sgemm_with_config(hta.KERNEL_VALU, nv, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
     assert r == hta.ERROR_INVALID_VALUE
     r = hta.mi_sgemm_with_config(5, 0, 0, 0, 4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
     assert r == hta.ERROR_INVALID_VALUE

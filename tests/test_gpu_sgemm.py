@@ -47,6 +47,8 @@ def run_kernel(kind, A, B, C, alpha, beta):
         hta.sgemm(A, B, C, alpha, beta, config=int(kind[len("mfma_cfg"):]))
     elif kind == "valu":
         hta.sgemm_valu(A, B, C, alpha, beta)
+    elif kind.startswith("valu_cfg"):
+        hta.sgemm_valu(A, B, C, alpha, beta, config=int(kind[len("valu_cfg"):]))
     elif kind == "splitk":
         hta.sgemm_splitk(A, B, C, alpha, beta, splits=0)
     elif kind.startswith("splitk_atomic"):
@@ -132,7 +134,8 @@ def whole_check(orc, kind, w, integer):
 # ---------------------------------------------------------------------------
 # Small ragged shapes on every path and every tile configuration
 # ---------------------------------------------------------------------------
-KINDS = (["mfma", "valu", "splitk", "splitk3", "splitk1", "splitk_atomic", "splitk_atomic3"]
+KINDS = (["mfma", "valu", "valu_cfg0", "valu_cfg1", "splitk", "splitk3", "splitk1",
+          "splitk_atomic", "splitk_atomic3"]
          + [f"mfma_cfg{i}" for i in range(N_MFMA_CFG)]
          + [f"splitk_cfg{i}" for i in range(N_MFMA_CFG)])
 SHAPES = [(1, 1, 1), (7, 9, 5), (33, 65, 17), (130, 257, 300), (255, 129, 64), (64, 128, 2049)]
