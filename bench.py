@@ -311,6 +311,47 @@ def secondary(kinds_workloads, seconds=0.25):
     return out
 
 
+def cold_secondary(kind="mfma", name="sgemm_2048x2048x2048", calls=40, flush_mib=512):
+    """One call at a time, each timed alone between HIP events, with the
+    operands out of every cache (a cold-cache run): before
+    each call a 512 MiB buffer, twice the 256 MB last-level cache, is
+    overwritten on the same stream.  The same single-call timing without the
+    flush is reported beside it, so that the difference is what the cold
+    caches cost (a single call also pays its own launch, which back-to-back
+    calls overlap)."""
+    import torch
+    import synth
+    from hpc_tiling_amd import perfmodel as pm
+    w = synth.workload(name)
+    host, dev, step = setup(w, kind)
+    buf = torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda:0")
+    warm(step, 3, 0.02)
+
+    def single_calls(flush):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(calls)]
+        for e0, e1 in evs:
+            if flush:
+                buf.fill_(1.0)
+            e0.record()
+            step()
+            e1.record()
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
+
+    rec = {"workload": name + " cold", "kernel": kind, "calls": calls,
+           "flush": f"{flush_mib} MiB overwritten before each call"}
+    for label, flush in (("cold", True), ("warm_single", False)):
+        secs = single_calls(flush)
+        med = secs[len(secs) // 2]
+        rec[label] = {"ms_per_call_median": 1e3 * med, "ms_per_call_min": 1e3 * secs[0],
+                      "ms_per_call_max": 1e3 * secs[-1], "tflops": w.flops / med / 1e12,
+                      "frac_of_fp32_peak": w.flops / med / pm.PEAK_FP32_MFMA}
+    del host, dev, step, buf
+    torch.cuda.empty_cache()
+    return rec
+
+
 def combine_secondary(name="sgemm_splitk_512x512x262144", seconds=0.25):
     """The split-K combine kernel alone, at the slice count the automatic
     plan uses for `name`: GB/s of its bytes 4 m n (S + 1) (S partial
@@ -474,6 +515,8 @@ def main(argv=None):
                     help="only time the FP32 FMA issue-rate probes (the VALU kernel's bound)")
     ap.add_argument("--combine-only", action="store_true",
                     help="only time the split-K combine kernel alone (for profiling)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="only time single 2048^3 calls with the caches flushed between them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="CSV",
@@ -526,6 +569,9 @@ def main(argv=None):
         return 0
     if args.combine_only:
         print(json.dumps({"combine": combine_secondary()}), flush=True)
+        return 0
+    if args.cold_only:
+        print(json.dumps({"cold": cold_secondary()}), flush=True)
         return 0
 
     import synth
@@ -622,6 +668,7 @@ def main(argv=None):
         line["secondary"] = secondary(pairs)
         line["secondary"].append(combine_secondary())
         line["secondary"].append(reduce_secondary())
+        line["secondary"].append(cold_secondary())
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
