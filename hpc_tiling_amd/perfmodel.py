@@ -14,13 +14,13 @@ PEAK_FP32_MFMA = 157.3e12      # dense FP32 matrix, 256 FLOP/clk/CU at 2.4 GHz
 PEAK_FP32_VECTOR = 157.3e12    # FP32 vector ALUs, 256 FLOP/clk/CU at 2.4 GHz
 # The VALU kernel's bound.  Built without packed FP32 instructions, its inner
 # loop is plain v_fma_f32 with every operand in a VGPR.  Measured on MI355X,
-# such an 8 x 8 register outer product sustains 137.7 TFLOP/s (0.875 of
-# 256 FLOP/clk/CU), while FMA chains with an SGPR operand sustain 76.7
-# (128 FLOP/clk/CU): the full vector rate, not half of it, bounds the loop.
+# such an 8 x 8 register outer product sustains 136-138 TFLOP/s over runs
+# (0.87 of 256 FLOP/clk/CU), while FMA chains with an SGPR operand sustain
+# 77 (128 FLOP/clk/CU): the full vector rate, not half of it, bounds the loop.
 PEAK_FP32_VALU = 157.3e12
 PEAK_FP32_VALU_NOTE = ("FP32 vector peak, 256 FLOP/clk/CU x 256 CUs x 2.4 GHz: plain v_fma_f32 "
                        "with VGPR operands issues at that rate (an 8x8 register outer product "
-                       "measured 137.7 TFLOP/s on MI355X)")
+                       "measured 136-138 TFLOP/s on MI355X)")
 PEAK_HBM_BYTES = 8.0e12        # HBM3E
 ELEM = 4                       # bytes per float
 
