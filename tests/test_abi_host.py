@@ -352,3 +352,25 @@ def test_tile_choice_rules():
     # the split-K entry's single-slice plans use the same choice
     p = hta.mi_sgemm_get_plan(hta.KERNEL_SPLITK, -1, 8192, 8192, 8192, 0)
     assert p["splits"] == 1 and (p["tile_m"], p["tile_k"], p["threads"]) == (128, 16, 512)
+
+
+@pytest.mark.parametrize("helper", ["sgemm", "sgemm_valu", "sgemm_splitk", "sgemm_streamk",
+                                    "sgemm_splitk_atomic"])
+def test_helpers_refuse_host_operands(helper):
+    """The torch helpers take device tensors only: a numpy array or a CPU
+    tensor is refused before any device call."""
+    import numpy as np
+    import torch
+    fn = getattr(hta, helper)
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        fn(np.zeros((2, 2), np.float32), torch.empty(2, 2))
+    with pytest.raises(ValueError, match="device tensor"):
+        fn(torch.empty(2, 2), torch.empty(2, 2))
+
+
+def test_reduce_sum_refuses_host_input():
+    import torch
+    with pytest.raises(TypeError, match="float32 device tensor"):
+        hta.reduce_sum(torch.ones(8))
+    with pytest.raises(TypeError, match="float32 device tensor"):
+        hta.reduce_sum([1.0, 2.0])

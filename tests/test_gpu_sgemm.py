@@ -370,3 +370,37 @@ def test_k_loop_endings(orc, config, aligned):
             lda, ldb = (k + 1 if (k + 1) % 4 else k + 2), n + 1
         w = synth.Workload(9, "kloop", m, n, k, lda, ldb, n + 3, "uniform", "int3", 1.5, -0.5)
         full_check(orc, f"mfma_cfg{config}", w, integer=True)
+
+
+def test_helper_argument_errors():
+    """The torch helpers refuse what the C ABI cannot take, before any
+    launch, and leave C untouched: wrong dtype, not 2-D, neither unit stride,
+    inner sizes that differ, a C of the wrong shape, beta != 0 without C, and
+    (VALU and atomic paths) a transposed view."""
+    say("helper argument errors")
+    A = torch.ones((8, 6), device="cuda")
+    B = torch.ones((6, 4), device="cuda")
+    C = torch.full((8, 4), 7.0, device="cuda")
+    for fn in (hta.sgemm, hta.sgemm_valu, hta.sgemm_splitk, hta.sgemm_streamk,
+               hta.sgemm_splitk_atomic):
+        with pytest.raises(TypeError, match="float32"):
+            fn(A.double(), B, C)
+        with pytest.raises(ValueError, match="2-D"):
+            fn(A.reshape(2, 4, 6), B, C)
+        with pytest.raises(ValueError):
+            fn(torch.ones((8, 12), device="cuda")[:, ::2], B, C)   # no unit stride
+        with pytest.raises(ValueError, match="inner sizes"):
+            fn(A, torch.ones((5, 4), device="cuda"), C)
+        with pytest.raises(ValueError, match="expected"):
+            fn(A, B, torch.empty((8, 5), device="cuda"))
+        with pytest.raises(ValueError, match="needs C"):
+            fn(A, B, None, 1.0, 0.5)
+    for fn in (hta.sgemm_valu, hta.sgemm_splitk_atomic):
+        with pytest.raises(ValueError, match="row-major"):
+            fn(torch.ones((6, 8), device="cuda").t(), B, C)
+    torch.cuda.synchronize()
+    assert torch.equal(C, torch.full((8, 4), 7.0, device="cuda")), "C written by a refused call"
+    # the transposed view is taken by the other entries
+    hta.sgemm(torch.ones((6, 8), device="cuda").t(), B, C)
+    torch.cuda.synchronize()
+    assert torch.equal(C, torch.full((8, 4), 6.0, device="cuda"))
